@@ -1,0 +1,152 @@
+/*
+ * sage.h -- C ABI of libsage, SageAttention's 8-bit attention forward pass
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [SA]  "SageAttention：低比特量化Attention，实现推理加速" -- section 技术方案:
+ *         item 1 smooth K (subtract its per-channel mean), item 2 per-block
+ *         INT8 quantisation of Q and K (INT32 accumulation of Q K^T), item 3
+ *         P.V kept in FP16 with an FP16 accumulator.
+ *   [SA2] "4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级" --
+ *         section 即插即用举例 (input Q, K, V; output O) and section 技术方案
+ *         item 4 (P and V quantised to FP8 E4M3).
+ *   [GUIDE] "如何将SageAttention量化注意力机制集成到你的AI项目中获得2-5倍速度提升"
+ *         -- section 针对不同AI任务的优化建议 (causal mode; varlen kernels).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Problem.  `nseq` sequences, `heads` heads, head dimension `head_dim` (64 or
+ *   128).  Dense problems (cu_seqlens == NULL) have nseq = batch and every
+ *   sequence of length max_seqlen.  Packed variable-length problems pass
+ *   `cu_seqlens`, a DEVICE array of nseq+1 int32 prefix offsets (cu[0] = 0,
+ *   non-decreasing, cu[nseq] = total_tokens); sequence s is tokens
+ *   [cu[s], cu[s+1]).  `max_seqlen` must be >= every length (the library
+ *   never reads cu_seqlens on the host).  Queries and keys are the same
+ *   tokens (self-attention).
+ * Tensors.  Element strides in a sage_strides {s, h, n}: element (seq s,
+ *   head h, token n, channel c) of a dense tensor is at s*S.s + h*S.h +
+ *   n*S.n + c; in a packed tensor it is at (cu[s] + n)*S.n + h*S.h + c
+ *   (S.s is ignored).  The channel stride is 1.  Base pointers must be
+ *   16-byte aligned and S.h, S.n multiples of 8 elements (fp16) / 16 (8-bit).
+ *   Q, K, V, O are fp16.  q8/k8 are int8; v8 is OCP FP8 E4M3 (uint8).
+ * Scales.  q_scale [nseq][heads][ceil(max_seqlen/blk_q)] and k_scale
+ *   [nseq][heads][ceil(max_seqlen/blk_k)] fp32, contiguous; entries past a
+ *   sequence's last block are left unspecified.  k_mean and v_scale are
+ *   [nseq][heads][head_dim] fp32, contiguous.
+ * Blocks.  blk_q and blk_k: quantisation block lengths in tokens, multiples
+ *   of 16 in [16, 256].  Blocks restart at each sequence's first token; the
+ *   last block of a sequence holds its remaining tokens.
+ * Ownership.  The caller allocates every buffer (device memory) including
+ *   the workspace; the library allocates and frees nothing on the device and
+ *   keeps no pointer after returning.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
+ *   is enqueued asynchronously; nothing synchronises.  Buffers must stay
+ *   valid until the stream has executed the work.
+ * Errors.  Every entry point returns a sage_status.  Arguments are checked
+ *   before anything is enqueued; on a non-OK status nothing was enqueued,
+ *   except SAGE_ERR_HIP, which reports a failed launch.  sage_last_error()
+ *   returns a thread-local message describing the last non-OK status.
+ *   Non-finite inputs are outside the contract.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = -1,
+  SAGE_ERR_UNSUPPORTED = -2,
+  SAGE_ERR_WORKSPACE = -3,
+  SAGE_ERR_HIP = -4
+} sage_status;
+
+typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 } sage_pv_mode;
+
+typedef struct {
+  int64_t s, h, n;
+} sage_strides;
+
+typedef struct {
+  int32_t nseq;               /* dense: batch; varlen: number of packed sequences */
+  int32_t heads;
+  int32_t max_seqlen;         /* dense: N; varlen: upper bound of every length    */
+  int32_t head_dim;           /* 64 or 128                                         */
+  int64_t total_tokens;       /* varlen: cu_seqlens[nseq]; dense: ignored          */
+  const int32_t* cu_seqlens;  /* device pointer, nseq+1 entries; NULL = dense      */
+  int32_t blk_q;              /* Q quantisation block (tokens)                     */
+  int32_t blk_k;              /* K quantisation block (tokens)                     */
+} sage_problem;
+
+/* Bytes of workspace sage_attn and sage_quantize need for this problem
+ * (sage_attn: int8 Q/K, their scales, mean(K), column-sum partials and, for
+ * SAGE_PV_FP8, the E4M3 V and its scales; sage_quantize: the column-sum
+ * partials only).  Writes *bytes; returns SAGE_OK or SAGE_ERR_INVALID_ARG. */
+int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes);
+int sage_quantize_workspace_bytes(const sage_problem* p, size_t* bytes);
+
+/* Smooth K and quantise Q and K to INT8 per block ([SA] 技术方案 items 1-2).
+ *   k_mean[s][h][c] = fp32( (sum over the sequence's tokens of K, exact) / L )
+ *   Q' = fp32(Q * sm_scale); K' = fp32(K - k_mean)
+ *   per block: scale = fp32(absmax / 127); code = round-half-even(fp32(x / scale)),
+ *   in [-127, 127]; an all-zero block has scale 0 and codes 0.
+ * sm_scale <= 0 selects fp32(1/sqrt(head_dim)).  q8 and k8 use the strides
+ * q8s, k8s (any layout, same indexing rules as the inputs).  `workspace`
+ * holds sage_quantize_workspace_bytes() bytes of scratch. */
+int sage_quantize(const sage_problem* p,
+                  const void* Q, sage_strides qs, const void* K, sage_strides ks, float sm_scale,
+                  int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s,
+                  float* q_scale, float* k_scale, float* k_mean,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* FP8 E4M3 V for the FP8 P.V path ([SA2] 技术方案 item 4):
+ *   v_scale[s][h][c] = fp32(max over the sequence's tokens of |V| / 448)
+ *   v8 = E4M3(fp32(V / v_scale)), round to nearest even, saturating at 448;
+ *   a channel that is all zero gets scale 0 and codes 0. */
+int sage_quantize_v_fp8(const sage_problem* p, const void* V, sage_strides vs,
+                        uint8_t* v8, sage_strides v8s, float* v_scale, void* stream);
+
+/* Fused attention over already-quantised inputs ([SA] 技术方案; [SA2] 即插即用举例):
+ *   S = (q8 . k8^T) * q_scale[block(i)] * k_scale[block(j)]   (INT32 accumulation)
+ *   keys of other sequences never count; causal keeps key j <= query i;
+ *   O = softmax(S) V, online softmax in fp32 (exp2), P.V on fp16 MFMA with
+ *   fp32 accumulation (pv_mode SAGE_PV_FP16, V fp16, v_scale unused) or on
+ *   FP8 MFMA with P as E4M3(448 * 2^(S log2e - m)), m the running row maximum
+ *   rounded up to an integer, and V = v8 with per-channel v_scale applied in
+ *   the epilogue (pv_mode SAGE_PV_FP8).  O is written as fp16 with strides os;
+ *   rows of a sequence of length 0 are not written. */
+int sage_attn_quantized(const sage_problem* p,
+                        const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
+                        const float* q_scale, const float* k_scale,
+                        const void* V, sage_strides vs, const float* v_scale,
+                        void* out, sage_strides os, int causal, int pv_mode, void* stream);
+
+/* The whole forward pass: sage_quantize (+ sage_quantize_v_fp8 in FP8 mode)
+ * into the workspace, then sage_attn_quantized.  O = softmax(Q K^T * sm_scale) V
+ * computed as described above.  `workspace` holds sage_workspace_bytes() bytes. */
+int sage_attn(const sage_problem* p,
+              const void* Q, sage_strides qs, const void* K, sage_strides ks,
+              const void* V, sage_strides vs, void* out, sage_strides os,
+              int causal, float sm_scale, int pv_mode,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Debug: the INT32 scores of the fused kernel's integer stage, written by
+ * the same MFMA code path before dequantisation.  Dense problems only, with
+ * max_seqlen <= 1024; s_out is int32 [nseq][heads][max_seqlen][max_seqlen]
+ * (query-major), every entry written. */
+int sage_debug_qk_i32(const sage_problem* p,
+                      const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
+                      int32_t* s_out, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* sage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H */

@@ -1,0 +1,298 @@
+// Pre-pass kernels of SageAttention's forward: smooth K, per-block INT8
+// quantisation of Q and K, and the E4M3 V of the FP8 P.V path.
+//
+// Pages followed:
+//   "SageAttention：低比特量化Attention，实现推理加速", section 技术方案,
+//     item 1: K minus its mean over tokens, one mean per channel;
+//     item 2: INT8 Q and K with one scale per block of rows (the attention
+//     kernel's tile size).
+//   "4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级", section
+//     技术方案 item 4: V quantised to FP8 E4M3.
+//
+// All of these are HBM-bound streaming passes.  Rounding is fixed so that the
+// results are bit-exact against a plain CPU implementation:
+//   * K column sums are taken in fp64; every fp16 value is a multiple of
+//     2^-24 and the sums stay far below 2^29, so each partial sum is exact
+//     and the result is independent of the reduction order.  mean =
+//     fp32(sum / L) with one IEEE fp64 division.
+//   * Q' = fp32(Q * sm_scale), K' = fp32(K - mean): one rounding each.
+//   * scale = fp32(absmax / 127) and code = rint(fp32(x / scale)) use IEEE
+//     fp32 division (HIP's default correctly rounded divide) and the
+//     hardware round-half-to-even; absmax is exact in any order.
+//   * E4M3 codes come from the hardware convert (round to nearest even).
+#include "sage_internal.h"
+
+namespace sage {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Block-wide max of a non-negative value (kThreads threads).
+__device__ __forceinline__ float block_max(float v) {
+  __shared__ float wm[kThreads / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = wm[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, wm[i]);
+  return r;
+}
+
+struct H8 {
+  _Float16 v[8];
+};
+
+__device__ __forceinline__ H8 load_h8(const _Float16* p) {
+  H8 r;
+  *reinterpret_cast<uint4*>(&r) = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+
+// ---------------------------------------------------------------- K column sums
+// grid (nchunk, heads, nseq): fp64 sums of K over one chunk of tokens.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_colsum(const _Float16* __restrict__ K, Str ks,
+                                                      const int32_t* __restrict__ cu, int max_seqlen,
+                                                      int nchunk, double* __restrict__ part) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = chunk * kColChunk;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + kColChunk);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const _Float16* base = K + seq_head_base(cu, ks, s, h) + cg * 8;
+  double acc[8] = {};
+#pragma unroll 4
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(base + (int64_t)n * ks.n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+  }
+  __shared__ double red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+    for (int i = 0; i < RPP; ++i) t += red[i][tid];
+    part[(((int64_t)s * H + h) * nchunk + chunk) * D + tid] = t;
+  }
+}
+
+// grid (heads, nseq), D threads: mean = fp32(sum / L).
+__global__ void k_mean_finalize(const double* __restrict__ part, const int32_t* __restrict__ cu, int max_seqlen,
+                       int nchunk, float* __restrict__ km) {
+  const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, D = blockDim.x, c = threadIdx.x;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int nc = (L + kColChunk - 1) / kColChunk;
+  double t = 0.0;
+  for (int k = 0; k < nc; ++k) t += part[(((int64_t)s * H + h) * nchunk + k) * D + c];
+  km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(t / (double)L) : 0.0f;
+}
+
+// ---------------------------------------------------------------- INT8 Q / K
+// grid (nbq + nbk, heads, nseq): one quantisation block of Q (x < nbq) or K.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_quant_qk(
+    const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks,
+    const int32_t* __restrict__ cu, int max_seqlen, int blk_q, int blk_k, int nbq, int nbk, float sm_scale,
+    const float* __restrict__ km, int8_t* __restrict__ q8, Str q8s, int8_t* __restrict__ k8, Str k8s,
+    float* __restrict__ sq, float* __restrict__ sk) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int b = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const bool isq = b < nbq;
+  const int blk = isq ? blk_q : blk_k;
+  const int bi = isq ? b : b - nbq;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = bi * blk;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + blk);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const Str xs = isq ? qs : ks;
+  const _Float16* src = (isq ? Q : K) + seq_head_base(cu, xs, s, h) + cg * 8;
+  float mean[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mean[i] = isq ? 0.0f : km[((int64_t)s * H + h) * D + cg * 8 + i];
+
+  auto transform = [&](float v, int i) -> float {
+    // one fp32 rounding: Q * sm_scale, or K - mean(K)
+    return isq ? v * sm_scale : v - mean[i];
+  };
+
+  float amax = 0.0f;
+#pragma unroll 2
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(src + (int64_t)n * xs.n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x.v[i], i)));
+  }
+  const float a = block_max(amax);
+  const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+  if (tid == 0) (isq ? sq : sk)[((int64_t)s * H + h) * (isq ? nbq : nbk) + bi] = scale;
+
+  const Str ds = isq ? q8s : k8s;
+  int8_t* dst = (isq ? q8 : k8) + seq_head_base(cu, ds, s, h) + cg * 8;
+#pragma unroll 2
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(src + (int64_t)n * xs.n);
+    uint32_t w[2] = {0u, 0u};
+    if (a > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float qv = rintf(transform((float)x.v[i], i) / scale);
+        qv = fminf(127.0f, fmaxf(-127.0f, qv));
+        w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (i & 3));
+      }
+    }
+    *reinterpret_cast<uint2*>(dst + (int64_t)n * ds.n) = make_uint2(w[0], w[1]);
+  }
+}
+
+// ---------------------------------------------------------------- E4M3 V
+// v_scale is first filled with 0, then each chunk folds its per-channel
+// max|V| in with an unsigned atomic max on the float bit pattern (for
+// non-negative floats the bit patterns order like the values, and max is
+// exact, so the result does not depend on the order), then k_v_scale divides
+// by 448 in place.
+__global__ void k_fill_zero(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.0f;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_v_colmax(const _Float16* __restrict__ V, Str vs,
+                                                        const int32_t* __restrict__ cu, int max_seqlen,
+                                                        float* __restrict__ vmax) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = chunk * kColChunk;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + kColChunk);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
+  float m[8] = {};
+#pragma unroll 4
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(base + (int64_t)n * vs.n);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf((float)x.v[i]));
+  }
+  __shared__ float red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = m[i];
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.0f;
+    for (int i = 0; i < RPP; ++i) t = fmaxf(t, red[i][tid]);
+    atomicMax(reinterpret_cast<unsigned int*>(vmax + ((int64_t)s * H + h) * D + tid), __float_as_uint(t));
+  }
+}
+
+__global__ void k_v_scale(float* __restrict__ sv, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sv[i] = sv[i] / 448.0f;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict__ V, Str vs,
+                                                       const int32_t* __restrict__ cu, int max_seqlen,
+                                                       const float* __restrict__ sv, uint8_t* __restrict__ v8,
+                                                       Str v8s) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = chunk * kColChunk;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + kColChunk);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const _Float16* src = V + seq_head_base(cu, vs, s, h) + cg * 8;
+  uint8_t* dst = v8 + seq_head_base(cu, v8s, s, h) + cg * 8;
+  float scale[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) scale[i] = sv[((int64_t)s * H + h) * D + cg * 8 + i];
+#pragma unroll 2
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(src + (int64_t)n * vs.n);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = scale[i] > 0.0f ? (float)x.v[i] / scale[i] : 0.0f;
+    uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    *reinterpret_cast<uint2*>(dst + (int64_t)n * v8s.n) = make_uint2(w0, w1);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+#define SAGE_DISPATCH_D(D_, ...)         \
+  do {                                   \
+    if ((D_) == 64) {                    \
+      constexpr int D = 64;              \
+      __VA_ARGS__;                       \
+    } else {                             \
+      constexpr int D = 128;             \
+      __VA_ARGS__;                       \
+    }                                    \
+  } while (0)
+
+hipError_t launch_k_colsum(const Problem& p, const void* K, Str ks, double* partial, hipStream_t st) {
+  dim3 grid(p.nchunk, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_colsum<D>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.nchunk, partial));
+  return hipGetLastError();
+}
+
+hipError_t launch_k_mean(const Problem& p, const double* partial, float* k_mean, hipStream_t st) {
+  hipLaunchKernelGGL(k_mean_finalize, dim3(p.heads, p.nseq), dim3(p.head_dim), 0, st, partial, p.cu, p.max_seqlen,
+                     p.nchunk, k_mean);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_qk(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                           const float* k_mean, int8_t* q8, Str q8s, int8_t* k8, Str k8s, float* q_scale,
+                           float* k_scale, hipStream_t st) {
+  dim3 grid(p.nbq + p.nbk, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim,
+                  hipLaunchKernelGGL((k_quant_qk<D>), grid, dim3(kThreads), 0, st, (const _Float16*)Q, qs,
+                                     (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.blk_k, p.nbq, p.nbk,
+                                     sm_scale, k_mean, q8, q8s, k8, k8s, q_scale, k_scale));
+  return hipGetLastError();
+}
+
+hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* vmax, hipStream_t st) {
+  const int64_t n = (int64_t)p.nseq * p.heads * p.head_dim;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vmax, n);
+  dim3 grid(p.nchunk, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colmax<D>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, vmax));
+  return hipGetLastError();
+}
+
+hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st) {
+  const int64_t n = (int64_t)p.nseq * p.heads * p.head_dim;
+  hipLaunchKernelGGL(k_v_scale, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v_scale, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, uint8_t* v8, Str v8s,
+                          hipStream_t st) {
+  dim3 grid(p.nchunk, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_v<D>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, v_scale, v8, v8s));
+  return hipGetLastError();
+}
+
+}  // namespace sage

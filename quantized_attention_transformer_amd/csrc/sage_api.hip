@@ -1,0 +1,280 @@
+// Host side of libsage: the C ABI declared in include/sage.h.
+//
+// Every entry point validates its arguments before anything is enqueued,
+// carves the caller's workspace, sizes the grids and enqueues the kernels on
+// the caller's stream.  Nothing here allocates device memory, synchronises or
+// reads device memory.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sage.h"
+#include "sage_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SAGE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_problem(const sage_problem* p) {
+  if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem is NULL");
+  if (p->nseq < 0 || p->heads <= 0 || p->max_seqlen < 0)
+    return fail(SAGE_ERR_INVALID_ARG, "nseq (%d) must be >= 0, heads (%d) > 0, max_seqlen (%d) >= 0", p->nseq,
+                p->heads, p->max_seqlen);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  for (int b : {p->blk_q, p->blk_k})
+    if (b < 16 || b > 256 || b % 16 != 0)
+      return fail(SAGE_ERR_INVALID_ARG, "blk_q/blk_k (%d, %d) must be multiples of 16 in [16, 256]", p->blk_q,
+                  p->blk_k);
+  if (p->cu_seqlens && p->total_tokens < 0) return fail(SAGE_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (p->heads > 65535 || p->nseq > 65535) return fail(SAGE_ERR_UNSUPPORTED, "heads and nseq must be <= 65535");
+  return SAGE_OK;
+}
+
+bool empty(const sage_problem* p) { return p->nseq == 0 || p->max_seqlen == 0; }
+
+sage::Problem to_internal(const sage_problem* p) {
+  sage::Problem q;
+  q.cu = p->cu_seqlens;
+  q.nseq = p->nseq;
+  q.heads = p->heads;
+  q.max_seqlen = p->max_seqlen;
+  q.head_dim = p->head_dim;
+  q.blk_q = p->blk_q;
+  q.blk_k = p->blk_k;
+  q.nbq = (int)cdiv(p->max_seqlen, p->blk_q);
+  q.nbk = (int)cdiv(p->max_seqlen, p->blk_k);
+  q.nchunk = (int)cdiv(p->max_seqlen, sage::kColChunk);
+  return q;
+}
+
+// Tensor check: non-null, 16-byte aligned, head and token strides multiples of `mult` elements.
+int check_tensor(const char* name, const void* ptr, sage_strides st, int mult, const sage_problem* p) {
+  if (!ptr) return fail(SAGE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(SAGE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  if (st.h % mult || st.n % mult || (!p->cu_seqlens && st.s % mult))
+    return fail(SAGE_ERR_INVALID_ARG, "%s strides (s=%lld h=%lld n=%lld) must be multiples of %d elements", name,
+                (long long)st.s, (long long)st.h, (long long)st.n, mult);
+  if (st.h < 0 || st.n < 0 || st.s < 0) return fail(SAGE_ERR_INVALID_ARG, "%s strides must be non-negative", name);
+  return SAGE_OK;
+}
+
+sage::Str S(sage_strides s) { return sage::Str{s.s, s.h, s.n}; }
+
+int64_t tokens(const sage_problem* p) {
+  return p->cu_seqlens ? p->total_tokens : (int64_t)p->nseq * p->max_seqlen;
+}
+
+// Workspace layout of sage_attn (offsets in bytes).  int8 Q/K (and E4M3 V)
+// are stored head-major: dense [nseq][heads][max_seqlen][d], packed
+// [heads][total_tokens][d].
+struct WsLayout {
+  size_t q8, k8, sq, sk, km, colsum, v8, sv, total;
+  sage_strides s8;
+};
+
+WsLayout ws_layout(const sage_problem* p, int pv_mode) {
+  const sage::Problem q = to_internal(p);
+  const int64_t T = tokens(p);
+  const int64_t d = p->head_dim, H = p->heads;
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  w.q8 = take((size_t)(T * H * d));
+  w.k8 = take((size_t)(T * H * d));
+  w.sq = take((size_t)p->nseq * H * q.nbq * 4);
+  w.sk = take((size_t)p->nseq * H * q.nbk * 4);
+  w.km = take((size_t)p->nseq * H * d * 4);
+  w.colsum = take((size_t)p->nseq * H * q.nchunk * d * 8);
+  if (pv_mode == SAGE_PV_FP8) {
+    w.v8 = take((size_t)(T * H * d));
+    w.sv = take((size_t)p->nseq * H * d * 4);
+  }
+  w.total = off;
+  if (p->cu_seqlens)
+    w.s8 = sage_strides{0, T * d, d};
+  else
+    w.s8 = sage_strides{H * p->max_seqlen * d, p->max_seqlen * d, d};
+  return w;
+}
+
+size_t quantize_ws_bytes(const sage_problem* p) {
+  const sage::Problem q = to_internal(p);
+  return align_up((size_t)p->nseq * p->heads * q.nchunk * p->head_dim * 8);
+}
+
+int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                 float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
+                 float* k_scale, float* k_mean, double* colsum, hipStream_t st) {
+  const sage::Problem q = to_internal(p);
+  if (sm_scale <= 0.0f || !std::isfinite(sm_scale)) sm_scale = (float)(1.0 / std::sqrt((double)p->head_dim));
+  hipError_t e;
+  if ((e = sage::launch_k_colsum(q, K, S(ks), colsum, st)) != hipSuccess) return hip_fail(e, "k_colsum launch");
+  if ((e = sage::launch_k_mean(q, colsum, k_mean, st)) != hipSuccess) return hip_fail(e, "k_mean launch");
+  if ((e = sage::launch_quant_qk(q, Q, S(qs), K, S(ks), sm_scale, k_mean, q8, S(q8s), k8, S(k8s), q_scale,
+                                 k_scale, st)) != hipSuccess)
+    return hip_fail(e, "quant_qk launch");
+  return SAGE_OK;
+}
+
+int run_quantize_v(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
+                   float* v_scale, hipStream_t st) {
+  const sage::Problem q = to_internal(p);
+  hipError_t e;
+  if ((e = sage::launch_v_colmax(q, V, S(vs), v_scale, st)) != hipSuccess) return hip_fail(e, "v_colmax launch");
+  if ((e = sage::launch_v_scale(q, v_scale, st)) != hipSuccess) return hip_fail(e, "v_scale launch");
+  if ((e = sage::launch_quant_v(q, V, S(vs), v_scale, v8, S(v8s), st)) != hipSuccess)
+    return hip_fail(e, "quant_v launch");
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_last_error(void) { return g_last_error.c_str(); }
+
+int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ws_layout(p, pv_mode).total;
+  return SAGE_OK;
+}
+
+int sage_quantize_workspace_bytes(const sage_problem* p, size_t* bytes) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = quantize_ws_bytes(p);
+  return SAGE_OK;
+}
+
+int sage_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                  float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
+                  float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
+      (rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)))
+    return rc;
+  if (!q_scale || !k_scale || !k_mean) return fail(SAGE_ERR_INVALID_ARG, "scale/mean outputs must not be NULL");
+  if (!workspace || workspace_bytes < quantize_ws_bytes(p))
+    return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, quantize_ws_bytes(p));
+  if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return run_quantize(p, Q, qs, K, ks, sm_scale, q8, q8s, k8, k8s, q_scale, k_scale, k_mean, (double*)workspace,
+                      (hipStream_t)stream);
+}
+
+int sage_quantize_v_fp8(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
+                        float* v_scale, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("v8", v8, v8s, 16, p))) return rc;
+  if (!v_scale) return fail(SAGE_ERR_INVALID_ARG, "v_scale is NULL");
+  return run_quantize_v(p, V, vs, v8, v8s, v_scale, (hipStream_t)stream);
+}
+
+int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8s, const int8_t* k8,
+                        sage_strides k8s, const float* q_scale, const float* k_scale, const void* V, sage_strides vs,
+                        const float* v_scale, void* out, sage_strides os, int causal, int pv_mode, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (empty(p)) return SAGE_OK;
+  const bool fp8 = pv_mode == SAGE_PV_FP8;
+  if ((rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)) ||
+      (rc = check_tensor("V", V, vs, fp8 ? 16 : 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
+    return rc;
+  if (!q_scale || !k_scale || (fp8 && !v_scale)) return fail(SAGE_ERR_INVALID_ARG, "scales must not be NULL");
+  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr};
+  hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, fp8, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return SAGE_OK;
+}
+
+int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks, const void* V,
+              sage_strides vs, void* out, sage_strides os, int causal, float sm_scale, int pv_mode, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
+      (rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
+    return rc;
+  const WsLayout w = ws_layout(p, pv_mode);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, w.total);
+  if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  int8_t* q8 = (int8_t*)(ws + w.q8);
+  int8_t* k8 = (int8_t*)(ws + w.k8);
+  float* sq = (float*)(ws + w.sq);
+  float* sk = (float*)(ws + w.sk);
+  if ((rc = run_quantize(p, Q, qs, K, ks, sm_scale, q8, w.s8, k8, w.s8, sq, sk, (float*)(ws + w.km),
+                         (double*)(ws + w.colsum), st)))
+    return rc;
+  const void* vin = V;
+  sage_strides vin_s = vs;
+  const float* sv = nullptr;
+  if (pv_mode == SAGE_PV_FP8) {
+    if ((rc = run_quantize_v(p, V, vs, (uint8_t*)(ws + w.v8), w.s8, (float*)(ws + w.sv), st)))
+      return rc;
+    vin = ws + w.v8;
+    vin_s = w.s8;
+    sv = (const float*)(ws + w.sv);
+  }
+  sage::AttnArgs a{q8, S(w.s8), k8, S(w.s8), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr};
+  hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode == SAGE_PV_FP8, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return SAGE_OK;
+}
+
+int sage_debug_qk_i32(const sage_problem* p, const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
+                      int32_t* s_out, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->cu_seqlens) return fail(SAGE_ERR_UNSUPPORTED, "sage_debug_qk_i32 supports dense problems only");
+  if (p->max_seqlen > 1024) return fail(SAGE_ERR_UNSUPPORTED, "sage_debug_qk_i32 supports max_seqlen <= 1024");
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p))) return rc;
+  if (!s_out || !aligned16(s_out)) return fail(SAGE_ERR_INVALID_ARG, "s_out must be non-NULL and 16-byte aligned");
+  if (p->max_seqlen % 4) return fail(SAGE_ERR_UNSUPPORTED, "sage_debug_qk_i32 needs max_seqlen % 4 == 0");
+  // scales are not read on the integer path
+  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), nullptr, nullptr, nullptr, sage::Str{0, 0, 0}, nullptr, nullptr,
+                   sage::Str{0, 0, 0}, s_out};
+  hipError_t e = sage::launch_attn(to_internal(p), a, false, false, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug qk launch");
+  return SAGE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal declarations shared by the libsage translation units (not part of
+// the C ABI).  Addressing follows sage.h: element (s, h, n, c) of a dense
+// tensor is at s*S.s + h*S.h + n*S.n + c, of a packed tensor at
+// (cu[s] + n)*S.n + h*S.h + c.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace sage {
+
+struct Str {
+  int64_t s, h, n;
+};
+
+// Tokens per partial of the column reductions (K sums, V absmax).
+constexpr int kColChunk = 512;
+
+__device__ __forceinline__ int seq_len(const int32_t* cu, int s, int max_seqlen) {
+  return cu ? (cu[s + 1] - cu[s]) : max_seqlen;
+}
+
+// Offset of token 0 of (sequence s, head h).
+__device__ __forceinline__ int64_t seq_head_base(const int32_t* cu, Str st, int s, int h) {
+  return (cu ? (int64_t)cu[s] * st.n : (int64_t)s * st.s) + (int64_t)h * st.h;
+}
+
+struct Problem {
+  const int32_t* cu;
+  int nseq, heads, max_seqlen, head_dim, blk_q, blk_k;
+  int nbq, nbk, nchunk;  // ceil(max_seqlen/blk_q), ceil(max_seqlen/blk_k), ceil(max_seqlen/kColChunk)
+};
+
+// ---- pre-pass (prepass.hip) ----
+hipError_t launch_k_colsum(const Problem& p, const void* K, Str ks, double* partial, hipStream_t st);
+hipError_t launch_k_mean(const Problem& p, const double* partial, float* k_mean, hipStream_t st);
+hipError_t launch_quant_qk(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                           const float* k_mean, int8_t* q8, Str q8s, int8_t* k8, Str k8s, float* q_scale,
+                           float* k_scale, hipStream_t st);
+// v_scale = max|V| / 448 per (sequence, head, channel): zero fill, atomic column max, divide in place.
+hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* v_scale, hipStream_t st);
+hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st);
+hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, uint8_t* v8, Str v8s,
+                          hipStream_t st);
+
+// ---- fused attention (attn_fwd.hip) ----
+struct AttnArgs {
+  const int8_t* q8;
+  Str q8s;
+  const int8_t* k8;
+  Str k8s;
+  const float* q_scale;
+  const float* k_scale;
+  const void* v;  // fp16 or E4M3
+  Str vs;
+  const float* v_scale;
+  void* out;  // fp16
+  Str os;
+  int32_t* dump;  // debug i32 scores or nullptr
+};
+hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
+
+}  // namespace sage

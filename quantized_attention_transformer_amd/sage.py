@@ -1,0 +1,211 @@
+"""Python binding of libsage (include/sage.h): argument marshalling only.
+
+Every computation runs in the HIP library; this module turns torch tensors
+(device memory) and torch's current stream into the C ABI's pointers,
+strides and stream handle.  It raises if libsage.so is missing or a call
+returns a non-OK status.
+
+Tensor layouts accepted: dense "bnhd" [B, N, H, d] (default) or "bhnd"
+[B, H, N, d]; packed variable-length [T, H, d] with cu_seqlens (int32,
+device).  The channel dimension must be contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsage.so")
+_lib = None
+
+SAGE_PV_FP16 = 0
+SAGE_PV_FP8 = 1
+
+EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quantize", "sage_quantize_v_fp8",
+            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_last_error")
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("nseq", ctypes.c_int32), ("heads", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("total_tokens", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
+                ("blk_q", ctypes.c_int32), ("blk_k", ctypes.c_int32)]
+
+
+class SageError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """Load libsage.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with quantized_attention_transformer_amd/build_lib.py")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, S, vp, i32, f32, sz = (ctypes.POINTER(Problem), Strides, ctypes.c_void_p, ctypes.c_int, ctypes.c_float,
+                                  ctypes.c_size_t)
+        L.sage_workspace_bytes.argtypes = [P, i32, ctypes.POINTER(sz)]
+        L.sage_quantize_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+        L.sage_quantize.argtypes = [P, vp, S, vp, S, f32, vp, S, vp, S, vp, vp, vp, vp, sz, vp]
+        L.sage_quantize_v_fp8.argtypes = [P, vp, S, vp, S, vp, vp]
+        L.sage_attn_quantized.argtypes = [P, vp, S, vp, S, vp, vp, vp, S, vp, vp, S, i32, i32, vp]
+        L.sage_attn.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp, sz, vp]
+        L.sage_debug_qk_i32.argtypes = [P, vp, S, vp, S, vp, vp]
+        L.sage_last_error.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name != "sage_last_error":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise SageError(fn, rc, lib().sage_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def strides_of(t: torch.Tensor, layout: str) -> Strides:
+    if t.stride(-1) != 1:
+        raise ValueError("the channel dimension must be contiguous")
+    if t.dim() == 3:                          # packed [T, H, d]
+        return Strides(0, t.stride(1), t.stride(0))
+    if layout == "bnhd":
+        return Strides(t.stride(0), t.stride(2), t.stride(1))
+    if layout == "bhnd":
+        return Strides(t.stride(0), t.stride(1), t.stride(2))
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def make_problem(q: torch.Tensor, layout: str = "bnhd", cu_seqlens: Optional[torch.Tensor] = None,
+                 max_seqlen: Optional[int] = None, blk_q: int = 128, blk_k: int = 64) -> Problem:
+    if cu_seqlens is not None:
+        if q.dim() != 3:
+            raise ValueError("packed inputs are [T, H, d]")
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens (the library never reads cu_seqlens on the host)")
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 device tensor")
+        return Problem(cu_seqlens.numel() - 1, q.shape[1], int(max_seqlen), q.shape[2], q.shape[0],
+                       cu_seqlens.data_ptr(), blk_q, blk_k)
+    if q.dim() != 4:
+        raise ValueError("dense inputs are 4-D")
+    B = q.shape[0]
+    N, H = (q.shape[1], q.shape[2]) if layout == "bnhd" else (q.shape[2], q.shape[1])
+    return Problem(B, H, N, q.shape[3], 0, None, blk_q, blk_k)
+
+
+def workspace_bytes(prob: Problem, pv_mode: int = SAGE_PV_FP16) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sage_workspace_bytes", lib().sage_workspace_bytes(ctypes.byref(prob), pv_mode, ctypes.byref(n)))
+    return n.value
+
+
+def quantize_workspace_bytes(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("sage_quantize_workspace_bytes", lib().sage_quantize_workspace_bytes(ctypes.byref(prob), ctypes.byref(n)))
+    return n.value
+
+
+def _nblocks(n, b):
+    return (n + b - 1) // b
+
+
+def quantize(q, k, *, sm_scale: Optional[float] = None, layout="bnhd", cu_seqlens=None, max_seqlen=None,
+             blk_q=128, blk_k=64, workspace=None):
+    """sage_quantize: returns dict(q8, k8 (int8, q's shape and layout), q_scale, k_scale, k_mean)."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    q8 = torch.empty(q.shape, dtype=torch.int8, device=q.device)
+    k8 = torch.empty(k.shape, dtype=torch.int8, device=q.device)
+    nseq, H, N, d = prob.nseq, prob.heads, prob.max_seqlen, prob.head_dim
+    sq = torch.zeros((nseq, H, _nblocks(N, blk_q)), dtype=torch.float32, device=q.device)
+    sk = torch.zeros((nseq, H, _nblocks(N, blk_k)), dtype=torch.float32, device=q.device)
+    km = torch.zeros((nseq, H, d), dtype=torch.float32, device=q.device)
+    nws = quantize_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().sage_quantize(ctypes.byref(prob), _ptr(q), strides_of(q, layout), _ptr(k), strides_of(k, layout),
+                             0.0 if sm_scale is None else float(sm_scale), _ptr(q8), strides_of(q8, layout),
+                             _ptr(k8), strides_of(k8, layout), _ptr(sq), _ptr(sk), _ptr(km), _ptr(workspace),
+                             workspace.numel(), _stream())
+    _check("sage_quantize", rc)
+    return dict(q8=q8, k8=k8, q_scale=sq, k_scale=sk, k_mean=km)
+
+
+def quantize_v_fp8(v, *, layout="bnhd", cu_seqlens=None, max_seqlen=None):
+    """sage_quantize_v_fp8: returns (v8 uint8 E4M3 codes in v's shape, v_scale [nseq, H, d])."""
+    prob = make_problem(v, layout, cu_seqlens, max_seqlen)
+    v8 = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    sv = torch.zeros((prob.nseq, prob.heads, prob.head_dim), dtype=torch.float32, device=v.device)
+    rc = lib().sage_quantize_v_fp8(ctypes.byref(prob), _ptr(v), strides_of(v, layout), _ptr(v8),
+                                   strides_of(v8, layout), _ptr(sv), _stream())
+    _check("sage_quantize_v_fp8", rc)
+    return v8, sv
+
+
+def attn_quantized(q8, k8, q_scale, k_scale, v, *, v_scale=None, causal=False, pv_mode=SAGE_PV_FP16,
+                   layout="bnhd", cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None):
+    """sage_attn_quantized: fused attention over quantised inputs; returns O (fp16, q8's shape)."""
+    prob = make_problem(q8, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.float16, device=q8.device)
+    rc = lib().sage_attn_quantized(ctypes.byref(prob), _ptr(q8), strides_of(q8, layout), _ptr(k8),
+                                   strides_of(k8, layout), _ptr(q_scale), _ptr(k_scale), _ptr(v),
+                                   strides_of(v, layout), _ptr(v_scale), _ptr(out), strides_of(out, layout),
+                                   int(bool(causal)), pv_mode, _stream())
+    _check("sage_attn_quantized", rc)
+    return out
+
+
+def attn(q, k, v, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAGE_PV_FP16, layout="bnhd",
+         cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None, workspace=None):
+    """sage_attn: the whole forward pass; returns O (fp16, q's shape)."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
+    nws = workspace_bytes(prob, pv_mode)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().sage_attn(ctypes.byref(prob), _ptr(q), strides_of(q, layout), _ptr(k), strides_of(k, layout),
+                         _ptr(v), strides_of(v, layout), _ptr(out), strides_of(out, layout), int(bool(causal)),
+                         0.0 if sm_scale is None else float(sm_scale), pv_mode, _ptr(workspace),
+                         workspace.numel(), _stream())
+    _check("sage_attn", rc)
+    return out
+
+
+def debug_qk_i32(q8, k8, *, layout="bnhd"):
+    """sage_debug_qk_i32: INT32 scores [B, H, N, N] from the fused kernel's integer stage."""
+    prob = make_problem(q8, layout)
+    s = torch.empty((prob.nseq, prob.heads, prob.max_seqlen, prob.max_seqlen), dtype=torch.int32,
+                    device=q8.device)
+    rc = lib().sage_debug_qk_i32(ctypes.byref(prob), _ptr(q8), strides_of(q8, layout), _ptr(k8),
+                                 strides_of(k8, layout), _ptr(s), _stream())
+    _check("sage_debug_qk_i32", rc)
+    return s
+
+
+def attention_ops(seqlens, heads: int, head_dim: int, causal: bool) -> float:
+    """Attention operation count used for TOPS: 4 * H * L^2 * d per sequence, halved when causal."""
+    tot = sum(4.0 * heads * float(L) * float(L) * head_dim for L in seqlens)
+    return tot / 2 if causal else tot
+
+
+def default_sm_scale(d: int) -> float:
+    return float(1.0 / math.sqrt(d))

@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/sage.h declares, and rejects bad arguments before enqueuing work
+(no HIP call is made on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_attention_transformer_amd import sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sage_quantize", "sage_attn", "sage_attn_quantized", "sage_quantize_v_fp8", "sage_debug_qk_i32",
+              "sage_workspace_bytes", "sage_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = sage.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(sage.EXPORTED)
+
+
+def _prob(**kw):
+    d = dict(nseq=1, heads=2, max_seqlen=256, head_dim=64, total_tokens=0, cu_seqlens=None, blk_q=64, blk_k=64)
+    d.update(kw)
+    return sage.Problem(**d)
+
+
+def _ws(p, mode=0):
+    n = ctypes.c_size_t(0)
+    rc = sage.lib().sage_workspace_bytes(ctypes.byref(p), mode, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_bytes_layout():
+    rc, n = _ws(_prob())
+    assert rc == 0
+    # int8 Q and K (2 x 32 KiB), scales, mean, fp64 column-sum partials; 256-byte aligned regions
+    assert n == 2 * 32768 + 256 + 256 + 512 + 1024
+    rc8, n8 = _ws(_prob(), 1)
+    assert rc8 == 0 and n8 == n + 32768 + 512
+    # quantize-only workspace: the column-sum partials
+    m = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_workspace_bytes(ctypes.byref(_prob()), ctypes.byref(m)) == 0
+    assert m.value == 1024
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), -2),
+    (dict(head_dim=0), -2),
+    (dict(blk_q=24), -1),
+    (dict(blk_k=512), -1),
+    (dict(blk_k=0), -1),
+    (dict(heads=0), -1),
+    (dict(nseq=-1), -1),
+    (dict(max_seqlen=-5), -1),
+])
+def test_problem_validation(kw, status):
+    rc, _ = _ws(_prob(**kw))
+    assert rc == status
+    assert sage.lib().sage_last_error().decode() != ""
+
+
+def test_null_problem_and_bad_mode():
+    n = ctypes.c_size_t(0)
+    assert sage.lib().sage_workspace_bytes(None, 0, ctypes.byref(n)) == -1
+    assert sage.lib().sage_workspace_bytes(ctypes.byref(_prob()), 7, ctypes.byref(n)) == -1
+
+
+FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _strides(s=256 * 2 * 64, h=64, n=128):
+    return sage.Strides(s, h, n)
+
+
+def test_attn_rejects_small_workspace():
+    p = _prob()
+    rc, need = _ws(p)
+    st = _strides()
+    r = sage.lib().sage_attn(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, st, FAKE, st, 0, 0.0, 0, FAKE, need - 1,
+                             None)
+    assert r == -3
+    assert "workspace" in sage.lib().sage_last_error().decode()
+
+
+def test_attn_rejects_null_and_misaligned():
+    p = _prob()
+    rc, need = _ws(p)
+    st = _strides()
+    r = sage.lib().sage_attn(ctypes.byref(p), None, st, FAKE, st, FAKE, st, FAKE, st, 0, 0.0, 0, FAKE, need, None)
+    assert r == -1 and "Q is NULL" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_attn(ctypes.byref(p), ctypes.c_void_p(0x10004), st, FAKE, st, FAKE, st, FAKE, st, 0, 0.0, 0,
+                             FAKE, need, None)
+    assert r == -1 and "aligned" in sage.lib().sage_last_error().decode()
+    bad = _strides(n=100)                 # token stride not a multiple of 8 elements
+    r = sage.lib().sage_attn(ctypes.byref(p), FAKE, bad, FAKE, st, FAKE, st, FAKE, st, 0, 0.0, 0, FAKE, need, None)
+    assert r == -1 and "strides" in sage.lib().sage_last_error().decode()
+
+
+def test_empty_problem_is_a_no_op():
+    p = _prob(max_seqlen=0)
+    st = _strides()
+    # nothing to do: OK without touching any pointer or the GPU
+    assert sage.lib().sage_attn(ctypes.byref(p), None, st, None, st, None, st, None, st, 1, 0.0, 0, None, 0,
+                                None) == 0
+    p = _prob(nseq=0)
+    assert sage.lib().sage_quantize(ctypes.byref(p), None, st, None, st, 0.0, None, st, None, st, None, None, None,
+                                    None, 0, None) == 0
+
+
+def test_debug_entry_limits():
+    p = _prob(max_seqlen=2048)
+    st = _strides()
+    assert sage.lib().sage_debug_qk_i32(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, None) == -2
+    cu = ctypes.c_void_p(0x20000)
+    p = _prob(cu_seqlens=cu.value, total_tokens=10)
+    assert sage.lib().sage_debug_qk_i32(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, None) == -2
+
+
+def test_binding_requires_max_seqlen_for_varlen():
+    import torch
+    q = torch.zeros((10, 2, 64), dtype=torch.float16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sage.make_problem(q, cu_seqlens=cu)
