@@ -1,0 +1,266 @@
+"""Benchmark of the SageAttention 8-bit attention forward on one MI355X.
+
+One step = the whole hot path on the text-LLM workload (B=1, H=8, N=4096,
+d=128, fp16 P.V, quantisation blocks 128 x 64) run twice, non-causal and
+causal: smooth K + INT8 Q/K (sage_quantize), then the fused attention kernel
+(sage_attn_quantized).  Inputs are synthetic (seeded, fp16, already resident
+in HBM before the timed region starts).
+
+value = attention TOPS of the step = (4 B H N^2 d + 4 B H N^2 d / 2) / t.
+roofline = the dominant kernel (the non-causal fused attention) against the
+MI355X dense INT8 MFMA peak; its duration is measured live with HIP events
+on the stream it runs on.  cpu_baseline = the CPU oracle on the same step.
+extra = kernel-only TOPS of the fused kernel on the larger workloads.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
+FP16_PEAK_TFLOPS = 2500.0
+METRIC = "attention TOPS (4·B·H·N²·d/t) at d=128, N=4K–32K; % of INT8 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_text_noncausal_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="first run a plain copy kernel of 256 MiB in / 256 MiB out (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "sage_internal.h"):
+        h.update(open(os.path.join(ROOT, "quantized_attention_transformer_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_or_null():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter runs, or None when the kernel source changed since they were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(attention shards by (sequence, head) with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_attention_transformer_amd import sage, synth
+    import ctypes
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    L = sage.lib()
+
+    wl = synth.TEXT
+    inp = synth.generate(wl)
+    B, N, H, d = inp.q.shape
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+    prob = sage.make_problem(q, "bnhd", blk_q=wl.blk_q, blk_k=wl.blk_k)
+    # int8 Q/K in head-major layout (the layout sage_attn uses for its workspace)
+    q8 = torch.empty((B, H, N, d), dtype=torch.int8, device=dev)
+    k8 = torch.empty((B, H, N, d), dtype=torch.int8, device=dev)
+    sq = torch.empty((B, H, -(-N // wl.blk_q)), dtype=torch.float32, device=dev)
+    sk = torch.empty((B, H, -(-N // wl.blk_k)), dtype=torch.float32, device=dev)
+    km = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, sage.quantize_workspace_bytes(prob)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    s_in, s8, so = sage.strides_of(q, "bnhd"), sage.strides_of(q8, "bhnd"), sage.strides_of(out, "bnhd")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.byref(prob)
+
+    def quantize():
+        rc = L.sage_quantize(P, q.data_ptr(), s_in, k.data_ptr(), s_in, 0.0, q8.data_ptr(), s8, k8.data_ptr(), s8,
+                             sq.data_ptr(), sk.data_ptr(), km.data_ptr(), ws.data_ptr(), ws.numel(), sp)
+        assert rc == 0, L.sage_last_error()
+
+    def attention(causal):
+        rc = L.sage_attn_quantized(P, q8.data_ptr(), s8, k8.data_ptr(), s8, sq.data_ptr(), sk.data_ptr(),
+                                   v.data_ptr(), s_in, None, out.data_ptr(), so, int(causal), 0, sp)
+        assert rc == 0, L.sage_last_error()
+
+    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for c in (False, True)}
+
+    def step(i=None):
+        for causal in (False, True):
+            quantize()
+            if i is not None:
+                ev[causal][i][0].record(stream)
+            attention(causal)
+            if i is not None:
+                ev[causal][i][1].record(stream)
+
+    if args.copy_calib:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)         # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    ops_nc = sage.attention_ops([N] * B, H, d, False)
+    ops_c = sage.attention_ops([N] * B, H, d, True)
+    value = (ops_nc + ops_c) / (ms_step * 1e-3) / 1e12
+    kern_nc = float(np.mean([a.elapsed_time(b) for a, b in ev[False]]))
+    kern_c = float(np.mean([a.elapsed_time(b) for a, b in ev[True]]))
+    achieved = ops_nc / (kern_nc * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+f16",
+        "data": "synthetic",
+        "config": {"workload": "text-LLM attention B1 H8 N4096 d128 fp16 P.V, blocks 128x64; one step = "
+                               "sage_quantize + fused attention, non-causal then causal",
+                   "batch": B, "heads": H, "seq_len": N, "head_dim": d, "blk_q": wl.blk_q, "blk_k": wl.blk_k,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_or_null(),
+                     "kernel": "fused attention, non-causal (k_attn<128,...,CAUSAL=false>)",
+                     "kernel_ms": round(kern_nc, 5), "causal_kernel_ms": round(kern_c, 5),
+                     "mixed_ceiling_frac": round(2 / 3, 4)},
+    }
+
+    if not args.no_extra:
+        result["extra"] = extra_workloads(sage, torch, dev)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, wl, ops_nc + ops_c)
+
+    print(json.dumps(result), flush=True)
+
+
+def extra_workloads(sage, torch, dev):
+    """Kernel-only TOPS of the fused attention on the larger workloads
+    (inputs drawn on the GPU with the workloads' distributions)."""
+    from quantized_attention_transformer_amd import synth
+    res = {}
+    g = torch.Generator(device=dev)
+    cases = [("long causal B1 H32 N32768 d128", synth.LONG, True, 0, None),
+             ("fp8-PV B4 H16 N8192 d128", synth.FP8, False, 1, None),
+             ("fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, None),
+             ("video B2 H24 N16384 d64", synth.VIDEO, False, 0, None),
+             ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen")]
+    for name, wl, causal, mode, kind in cases:
+        g.manual_seed(wl.seed)
+        if kind == "varlen":
+            import numpy as np
+            lens = synth.draw_varlen_lengths(np.random.default_rng(wl.seed), wl.varlen_nseq, wl.varlen_min,
+                                             wl.varlen_max, wl.varlen_total_max)
+            T = int(lens.sum())
+            shape = (T, wl.heads, wl.head_dim)
+            cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=dev)
+            kw = dict(cu_seqlens=cu, max_seqlen=int(lens.max()))
+            seqlens = lens.tolist()
+        else:
+            shape = (wl.batch, wl.seqlen, wl.heads, wl.head_dim)
+            kw = {}
+            seqlens = [wl.seqlen] * wl.batch
+        q = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
+        bias = torch.randn((wl.heads, wl.head_dim), generator=g, device=dev) * wl.bias_std
+        k = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) + bias).half()
+        v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
+        qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
+        vv, sv = (sage.quantize_v_fp8(v, **kw) if mode == 1 else (v, None))
+        out = torch.empty_like(q)
+
+        def run():
+            sage.attn_quantized(qd["q8"], qd["k8"], qd["q_scale"], qd["k_scale"], vv, v_scale=sv, causal=causal,
+                                pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out, **kw)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        n = 5
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        ops = sage.attention_ops(seqlens, wl.heads, wl.head_dim, causal)
+        tops = ops / (ms * 1e-3) / 1e12
+        res[name] = {"kernel_ms": round(ms, 4), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+        del q, k, v, qd, vv, out
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(inp, wl, ops):
+    """The CPU oracle (as it stands) on the same step: quantisation and fp64
+    attention, non-causal then causal, full workload."""
+    from oracle import sage_oracle as O
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:                      # pragma: no cover
+        threadpool_limits, threadpool_info = None, None
+    cores = min(16, len(os.sched_getaffinity(0)))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        t = time.perf_counter()
+        for causal in (False, True):
+            O.sage_attn(inp.q, inp.k, inp.v, inp.seqlens, None, causal, wl.blk_q, wl.blk_k)
+        dt = time.perf_counter() - t
+        used = cores
+        if threadpool_info:
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": used, "kind": "oracle",
+            "sample": f"the full step (B1 H8 N4096 d128, quantise + attention, non-causal and causal) in "
+                      f"{dt:.1f} s; matrix products on {used} BLAS threads, elementwise work single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -81,6 +81,14 @@ int check_tensor(const char* name, const void* ptr, sage_strides st, int mult, c
 
 sage::Str S(sage_strides s) { return sage::Str{s.s, s.h, s.n}; }
 
+// The attention kernel addresses one (sequence, head) of K and V through a
+// buffer resource with 32-bit offsets: max_seqlen rows must span < 2 GiB.
+int check_row_span(const char* name, sage_strides st, int elem_bytes, const sage_problem* p) {
+  if ((int64_t)p->max_seqlen * st.n * elem_bytes >= (int64_t)1 << 31)
+    return fail(SAGE_ERR_UNSUPPORTED, "%s: max_seqlen * token stride must stay below 2 GiB", name);
+  return SAGE_OK;
+}
+
 int64_t tokens(const sage_problem* p) {
   return p->cu_seqlens ? p->total_tokens : (int64_t)p->nseq * p->max_seqlen;
 }
@@ -214,6 +222,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
       (rc = check_tensor("V", V, vs, fp8 ? 16 : 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
     return rc;
   if (!q_scale || !k_scale || (fp8 && !v_scale)) return fail(SAGE_ERR_INVALID_ARG, "scales must not be NULL");
+  if ((rc = check_row_span("k8", k8s, 1, p)) || (rc = check_row_span("V", vs, fp8 ? 1 : 2, p))) return rc;
   sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -230,6 +239,7 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
       (rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
     return rc;
+  if ((rc = check_row_span("V", vs, 2, p))) return rc;
   const WsLayout w = ws_layout(p, pv_mode);
   if (!workspace || workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, w.total);
