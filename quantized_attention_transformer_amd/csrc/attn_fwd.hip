@@ -10,12 +10,14 @@
 //   "如何将SageAttention量化注意力机制集成到你的AI项目中获得2-5倍速度提升",
 //     section 针对不同AI任务的优化建议: causal mode and packed varlen sequences.
 //
-// Work decomposition.  One workgroup = 4 waves x 32 query rows of one
-// (sequence, head); it walks 64-key tiles of K and V through three LDS
-// stages, filled straight from global memory by buffer_load ... lds.
-// (Sequence, head) pairs are dealt round-robin over the 8 XCDs and each XCD
-// runs all query tiles of a pair back to back (longest causal rows first), so
-// a pair's K/V re-reads stay in one L2 and the work spreads evenly.
+// Work decomposition.  One workgroup = 128 query rows of one (sequence,
+// head), 8 waves in two halves of 4.  Wave w of half h owns rows 32(w%4) ..
+// 32(w%4)+31 and the 64-key tiles t = h, h+2, h+4, ...: the halves split the
+// keys and merge their partial (O, l, m) through LDS at the end.  The two
+// waves a SIMD hosts (w and w+4) belong to different halves.  (Sequence,
+// head) pairs are dealt round-robin over the 8 XCDs and each XCD runs all
+// query tiles of a pair back to back (longest causal rows first), so a pair's
+// K/V re-reads stay in one L2 and the work spreads evenly.
 //
 // Per 64-key tile, on the matrix cores (one wave, 32 rows):
 //   S^T[key][query] += K[key][c] . Q[query][c]   v_mfma_i32_32x32x32_i8 (8x)
@@ -35,21 +37,29 @@
 //         read (two reads per operand);
 //   fp8:  V is written to LDS transposed ([channel][permuted key]).
 //
-// Software pipeline (per wave, step t): the P.V MFMAs of tile t-1 run while
-// the VALU computes the softmax of tile t; one barrier; the loads of tile t+2
-// are issued and the INT8 MFMAs of tile t+1.  The matrix cores see QK(t+1)
-// then PV(t) back to back while the softmax of tile t+1 overlaps PV(t).
+// Ping-pong schedule.  Time is cut into phases b = 0, 1, ..., ntiles+1, one
+// workgroup barrier after each.  In phase b the half with h = b mod 2 is in
+// its matrix phase: INT8 S of tile b and the P.V of tile b-2; the other half
+// is in its vector phase: the softmax of tile b-1.  So at any time one wave
+// of every SIMD feeds the matrix core while the other keeps the VALU busy,
+// and S and P need one register set each.  At the start of phase b every
+// wave issues its share of the loads of tile b+2 (K straight into LDS with
+// buffer_load ... lds; fp16 V too, E4M3 V through registers so it can be
+// transposed).  K tiles live in a ring of 3 LDS slots (read in phase t), V
+// tiles in a ring of 5 (read in phase t+2).
 //
 // Softmax.  The i32 accumulator starts at the bit pattern of 1.5*2^23, so the
 // MFMA leaves the float 1.5*2^23 + S exactly (|S| <= 127^2*128 < 2^22): no
 // conversion instruction.  With c = q_scale*k_scale*log2(e) the exponent is
-// one FMA, x*c - (1.5*2^23*c + m).  m is the running row maximum in base-2
-// units; O and l are rescaled (wave-uniform branch) only when some row's
-// maximum grows: by more than 8 on the fp16 path (P stays <= 2^8, exact in
-// fp16), by any amount on the FP8 path, where m is kept rounded up to an
-// integer so rescales are exact powers of two and E4M3(448 p) does not depend
-// on the order keys are visited.  l sums the fp16-rounded P fed to the MFMA
-// (v_dot2) on the fp16 path, and the unquantised P on the FP8 path.
+// one FMA, x*c - (1.5*2^23*c + m).  fp16 path: m is a lazy running row
+// maximum in base-2 units (moved only when the tile maximum exceeds it by
+// more than 8; P <= 2^8 is exact in fp16), O rescaled by 2^(m_old - m_new)
+// when it moves (rare).  FP8 path: m is kept rounded up to an integer
+// (E4M3(448 p) then does not depend on the order keys are visited) and O is
+// not rescaled: it keeps the first tile's maximum m0 as reference and each
+// tile's P enters the P.V MFMA with the exact per-lane E8M0 scale
+// 2^(m - m0).  l sums the fp16-rounded P fed to the MFMA (v_dot2) on the
+// fp16 path, the unquantised P on the FP8 path.
 #include <type_traits>
 
 #include "sage_internal.h"
@@ -73,28 +83,36 @@ constexpr float kLog2_448 = 8.807354922057604f;
 constexpr int kMagicBits = 0x4B400000;  // float 1.5 * 2^23
 constexpr float kMagic = 12582912.0f;
 constexpr int BN = 64;                  // keys per tile
-constexpr int NW = 4;                   // waves per workgroup
+constexpr int NW = 8;                   // waves per workgroup (two halves of 4)
 constexpr int NT = NW * 64;
-constexpr int BM = NW * 32;             // query rows per workgroup
+constexpr int BM = 128;                 // query rows per workgroup (32 per wave of a half)
+constexpr int NSK = 3;                  // K ring slots
+constexpr int NSV = 5;                  // V ring slots
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9 (raw, 32-bit format)
 
-// LDS stage of one 64-key tile.  K rows (D bytes) and fp16 V rows (2D bytes)
-// are stored without padding; 16-byte chunks are XOR-swizzled by row so that
+// LDS of one workgroup.  K rows (D bytes) and fp16 V rows (2D bytes) are
+// stored without padding; 16-byte chunks are XOR-swizzled by row so that
 // every 256-byte LDS pass of the fragment reads (64 banks x 4 B) hits each
 // bank once:
 //   K:  chunk c of row r at c ^ ((r / (256/D)) % (D/16))   (ds_read_b128, 16 lanes = 16 rows)
 //   V:  chunk c of row r at c ^ 4*(r % 4)       (D = 128)  (ds_read_b64_tr_b16, 32 lanes =
 //                           c ^ 4*((r / 2) % 2) (D = 64)    4 rows x 64 bytes)
 // The E4M3 V is stored transposed ([channel][permuted key], rows of BN+16 bytes).
+// After the key loop the same bytes hold the second half's partial results.
 template <int D, bool FP8>
 struct Lds {
   static constexpr int KBYTES = BN * D;
   static constexpr int VROW = FP8 ? (BN + 16) : 2 * D;
   static constexpr int VBYTES = (FP8 ? D : BN) * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int NSTAGE = 3;
-  static constexpr int KBLK = KBYTES / 1024 / NW;             // 1 KiB DMA blocks per wave (K)
-  static constexpr int VBLK = FP8 ? 0 : VBYTES / 1024 / NW;   // (fp16 V)
+  static constexpr int VRING = NSK * KBYTES;  // offset of the V ring
+  static constexpr int RING = VRING + NSV * VBYTES;
+  static constexpr int MSTRIDE = D / 2 + 2;   // floats per lane of a partial result: O^T, m, l
+  static constexpr int MERGE = 4 * MSTRIDE * 64 * 4;
+  static constexpr int KSTAB = RING > MERGE ? RING : MERGE;  // per-tile k_scale table (key blocks of 64k keys)
+  static constexpr int KSCAP = 4096;                          // its capacity in tiles
+  static constexpr int BYTES = KSTAB + 4 * KSCAP;
+  static constexpr int KCH = KBYTES / 1024;             // 1 KiB DMA blocks per K tile
+  static constexpr int VCH = FP8 ? 0 : VBYTES / 1024;   // (fp16 V)
   __device__ static constexpr int kswz(int r) { return (r / (256 / D)) % (D / 16); }
   __device__ static constexpr int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
@@ -103,25 +121,53 @@ __device__ __forceinline__ int pos8(int kq) {  // byte position of key quad kq i
   return 32 * (kq & 1) + 16 * (kq >> 3) + 4 * ((kq & 7) >> 1);
 }
 
-// Per-lane constants of the direct-to-LDS tile loads.  Wave w fills 1 KiB
-// blocks w*NBLK .. w*NBLK+NBLK-1 of a region; lane l lands at block + 16 l and
-// fetches the global 16-byte chunk the swizzle assigns there, at byte offset
-// (row within the tile) * row_stride + 16 * chunk.
+// Buffer descriptor (gfx9 raw buffer): base, num_records bytes, stride 0.
+__device__ __forceinline__ v4i make_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), bytes, kRsrcWord3};
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS at lds_addr +
+// 16 * lane (buffer_load_dwordx4 ... lds).  Written as inline asm: these loads
+// write no register, and hiding them from the compiler keeps it from waiting
+// for every one of them before each later LDS read.  The caller orders them
+// with explicit s_waitcnt vmcnt and a barrier before the data is read.  M0
+// (the LDS base of the load) is saved and restored around it.
+__device__ __forceinline__ void dma_b128(const v4i& rsrc, int voff, uint32_t lds_addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %1, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(rsrc), "v"(voff), "s"(lds_addr)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+
+// Per-lane constants of the direct-to-LDS tile loads.  Wave w fills the 1 KiB
+// blocks w, w+NW, ... of a tile; lane l lands at block + 16 l and fetches the
+// global 16-byte chunk the swizzle assigns there, at byte offset (row within
+// the tile) * row_stride + 16 * chunk.
 template <int D, bool FP8>
 struct DmaPlan {
   using S = Lds<D, FP8>;
-  int koff[S::KBLK];
-  int voff[S::VBLK > 0 ? S::VBLK : 1];
+  static constexpr int KPW = (S::KCH + NW - 1) / NW;  // K blocks per wave (some waves may have none)
+  static constexpr int VPW = S::VCH / NW;             // fp16 V blocks per wave
+  int koff[KPW];
+  int voff[VPW > 0 ? VPW : 1];
   __device__ void init(int w, int lane, int64_t kn, int64_t vn) {
 #pragma unroll
-    for (int x = 0; x < S::KBLK; ++x) {
-      const int byte = (w * S::KBLK + x) * 1024 + 16 * lane;
+    for (int x = 0; x < KPW; ++x) {
+      const int byte = (w + NW * x) * 1024 + 16 * lane;
       const int r = byte / D, c = ((byte % D) / 16) ^ S::kswz(r);
       koff[x] = (int)(r * kn) + 16 * c;
     }
 #pragma unroll
-    for (int x = 0; x < S::VBLK; ++x) {
-      const int byte = (w * S::VBLK + x) * 1024 + 16 * lane;
+    for (int x = 0; x < VPW; ++x) {
+      const int byte = (w + NW * x) * 1024 + 16 * lane;
       const int r = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ S::vswz(r);
       voff[x] = (int)(r * vn) + 16 * c;
     }
@@ -129,20 +175,15 @@ struct DmaPlan {
   // One tile: the descriptors start at the tile's first row and end at the
   // sequence's last byte, so rows past the sequence fall outside them (their
   // LDS bytes keep older, finite, data; those keys are masked).
-  __device__ __forceinline__ void issue(const int8_t* kseq, int64_t kn, const uint8_t* vseq, int64_t vn, int j0,
-                                        int L, lds_u8* stage, int w) const {
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kseq + (int64_t)j0 * kn), 0, (int)((L - 1 - j0) * kn + D), kRsrcWord3);
+  __device__ __forceinline__ void issue_k(const v4i& kr, lds_u8* slot, int w) const {
 #pragma unroll
-    for (int x = 0; x < S::KBLK; ++x)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (LDS void*)(stage + (w * S::KBLK + x) * 1024), 16, koff[x], 0, 0, 0);
-    if constexpr (S::VBLK > 0) {
-      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(vseq + (int64_t)j0 * vn), 0, (int)((L - 1 - j0) * vn + 2 * D), kRsrcWord3);
+    for (int x = 0; x < KPW; ++x)
+      if (S::KCH % NW == 0 || w + NW * x < S::KCH) dma_b128(kr, koff[x], lds_addr(slot + (w + NW * x) * 1024));
+  }
+  __device__ __forceinline__ void issue_v(const v4i& vr, lds_u8* slot, int w) const {
+    if constexpr (VPW > 0) {
 #pragma unroll
-      for (int x = 0; x < S::VBLK; ++x)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (LDS void*)(stage + S::KBYTES + (w * S::VBLK + x) * 1024), 16,
-                                                 voff[x], 0, 0, 0);
+      for (int x = 0; x < VPW; ++x) dma_b128(vr, voff[x], lds_addr(slot + (w + NW * x) * 1024));
     }
   }
 };
@@ -201,21 +242,19 @@ struct V8Stager {
 };
 
 // S^T for one 64-key tile: s[jt] (keys 32jt..32jt+31) = 1.5*2^23 + K . Q^T (as int
-// bits); `magic` (all lanes 0x4B400000) is the first MFMA's accumulator input.
-// kl: this lane's K row li; kx[kk]: swizzled byte offset of chunk 2kk+g in it.
+// bits); `magic` (0x4B400000 in every lane) is the first MFMA's accumulator input.
+// kx[kk]: byte offset in a K slot of chunk 2kk+g (swizzled) of this lane's row li.
 template <int D>
-__device__ __forceinline__ void qk_tile(const lds_u8* kl, const int (&kx)[D / 32], const v4i (&qf)[D / 32],
+__device__ __forceinline__ void qk_tile(const lds_u8* kslot, const uint32_t (&kx)[D / 32], const v4i (&qf)[D / 32],
                                         const v16i& magic, v16i (&s)[2]) {
-  v4i kf[2][D / 32];
-#pragma unroll
-  for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) kf[jt][kk] = *(const LDS v4i*)(kl + 32 * jt * D + kx[kk]);
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
-    v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
+    v4i kf[D / 32];
 #pragma unroll
-    for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
+    for (int kk = 0; kk < D / 32; ++kk) kf[kk] = *(const LDS v4i*)(kslot + kx[kk] + 32 * jt * D);
+    v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0], qf[0], magic, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kk], qf[kk], acc, 0, 0, 0);
     s[jt] = acc;
   }
 }
@@ -227,17 +266,6 @@ __device__ __forceinline__ float xhalf_max(float v) {  // max over lanes l and l
 __device__ __forceinline__ float xhalf_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// x *= a in place (a tied register operand keeps the accumulator where the
-// MFMAs expect it on both sides of the rescale branch).
-__device__ __forceinline__ void scale_inplace(v16f& x, float a) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float t = x[r];
-    asm volatile("v_mul_f32 %0, %1, %0" : "+v"(t) : "v"(a));
-    x[r] = t;
-  }
 }
 
 template <int D, bool FP8, bool CAUSAL, bool KSU>
@@ -258,15 +286,17 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   if (q0 >= L) return;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = w >> 2;  // half: key tiles t = hf (mod 2)
 
   const int8_t* __restrict__ qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h);
   const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, h);
   const uint8_t* vseq = (const uint8_t*)a.v + seq_head_base(p.cu, a.vs, s, h) * (FP8 ? 1 : 2);
   const int64_t kn = a.k8s.n, vn = a.vs.n * (FP8 ? 1 : 2);  // row strides in bytes
   const float* __restrict__ ksc = a.k_scale + sh * p.nbk;
+  const __attribute__((address_space(4))) float* ksc_c = (const __attribute__((address_space(4))) float*)ksc;
 
   // ---- this lane's query row and its Q fragments (B operand of S^T)
-  const int row0 = q0 + w * 32;
+  const int row0 = q0 + (w & 3) * 32;
   const int i = row0 + li;
   v4i qf[D / 32];
   float qsc = 0.0f;
@@ -289,21 +319,24 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int wtiles = CAUSAL ? min(ntiles, (row0 + 31) / BN + 1) : ntiles;
 
   // LDS fragment offsets of this lane: K row li, chunk 2kk+g (swizzled) ...
-  int kx_off[D / 32];
+  uint32_t kofs[D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kx_off[kk] = 16 * ((2 * kk + g) ^ S::kswz(li));
-  const int krow = li * D;
+  for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * D + 16 * ((2 * kk + g) ^ S::kswz(li));
+  const uint32_t vrow8 = li * S::VROW + 32 * g;  // FP8: this lane's V^T row and half
   // ... and the transposed fp16 V reads: rows 4g + tl/4 (+8), chunk 4ct + 2(b&1) + (tl&3)/2
   const int vb = lane >> 4, tl = lane & 15;
   int vaddr[D / 32];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) {
     const int vr = 4 * g + (tl >> 2);
-    vaddr[ct] = S::KBYTES + vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
+    vaddr[ct] = vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
   }
 
   // LDS starts zeroed so bytes the tail tiles leave untouched are finite.
-  for (int x = tid; x < S::NSTAGE * S::STAGE / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
+  for (int x = tid; x < S::RING / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
+  const bool ks_in_lds = KSU && ntiles <= S::KSCAP;
+  if (ks_in_lds)
+    for (int t = tid; t < ntiles; t += NT) *(LDS float*)(lds + S::KSTAB + 4 * t) = ksc[(t * BN) / p.blk_k];
   __syncthreads();
 
   DmaPlan<D, FP8> dma;
@@ -311,61 +344,86 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   V8Stager<D> v8s;
 
   float m = -INFINITY, lsum = 0.0f;
+  // FP8: O and l accumulate relative to the first tile's maximum m0; tile t's
+  // P (E4M3, relative to the running integer maximum m) enters the P.V MFMA
+  // with the exact per-lane E8M0 factor 2^(m - m0), so O is rarely rescaled.
+  float m0 = 0.0f;
+  int pscale = 127;
   v16f o[D / 32];
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct) o[ct] = v16f{};
-  v16i sc[2];        // S of the tile being softmaxed
-  v8h pf[4], pfp[4];  // fp16 P of this tile / of the previous tile
-  v8i pf8, pf8p;      // E4M3 P of this tile / of the previous tile
+  v16i sc[2];   // S of the tile between its matrix and vector phases
+  v8h pf[4];    // fp16 P (between the vector phase and the next matrix phase)
+  v8i pf8;      // E4M3 P
 
-  // O^T += V^T . P^T for the tile in stage `st` (P from the previous step)
-  auto pv = [&](const lds_u8* st) {
+  // O^T += V^T . P^T for the tile at LDS byte offset vso
+  auto pv = [&](uint32_t vso) {
     if constexpr (!FP8) {
+      uint32_t va[D / 32];
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct) va[ct] = vso + vaddr[ct];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) {
-          const lds_u8* pa = st + vaddr[ct] + 16 * u * S::VROW;
+          const lds_u8* pa = lds + va[ct] + 16 * u * S::VROW;
           const v4h ha = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)pa));
           const v4h hb = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)(pa + 8 * S::VROW)));
           const v8h vf = __builtin_shufflevector(ha, hb, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pfp[u], o[ct], 0, 0, 0);
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], o[ct], 0, 0, 0);
         }
       }
     } else {
-      const lds_u8* vl = st + S::KBYTES + li * S::VROW + 32 * g;  // V^T rows = channels
+      const lds_u8* vl = lds + (vso + vrow8);  // V^T rows = channels
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct) {
         const lds_u8* pa = vl + 32 * ct * S::VROW;
         const v4i va = *(const LDS v4i*)(pa);
         const v4i vb2 = *(const LDS v4i*)(pa + 16);
         const v8i vf = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf8p, o[ct], 0, 0, 0, 127, 0, 127);
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf8, o[ct], 0, 0, 0, 127, 0, pscale);
       }
     }
   };
 
-  // softmax of tile t from sc -> pf / pf8 (lane: row i, keys j(jt, r)).
-  // MASKED tiles (sequence tail, causal diagonal) take a separate instantiation.
-  auto softmax = [&](int t, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  // k_scale * q_scale * log2(e) for the keys of tile t this lane handles
+  // (per (jt, group of 4 keys); one value when key blocks are multiples of
+  // the tile).  Loaded before the phase's tile loads are issued so that waiting
+  // for it does not wait for them.
+  struct Ck {
+    float c[2][4];
+  };
+  auto load_ck = [&](int t) {
+    Ck ck;
     const int j0 = t * BN;
-    float c[2][4];  // q_scale * k_scale * log2(e) per (jt, group of 4 keys)
     if constexpr (KSU) {
-      const float ck = qsc * ksc[j0 / p.blk_k];
+      // one value per tile, from the LDS table (longer sequences: a scalar
+      // load, counted by lgkmcnt rather than by the tile loads' vmcnt)
+      const float v = qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
+                                       : ksc_c[min(j0, L - 1) / p.blk_k]);
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c[jt][q] = ck;
+        for (int q = 0; q < 4; ++q) ck.c[jt][q] = v;
     } else {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int j = j0 + 32 * jt + 8 * q + 4 * g;
-          c[jt][q] = j < L ? qsc * ksc[j / p.blk_k] : 0.0f;
+          const float v = ksc[min(j, L - 1) / p.blk_k];  // unconditional: one batch of loads, one wait
+          ck.c[jt][q] = j < L ? qsc * v : 0.0f;
         }
     }
+    return ck;
+  };
+
+  // softmax of tile t from sc -> pf / pf8 (lane: row i, keys j(jt, r)).
+  // MASKED tiles (sequence tail, causal diagonal) take a separate instantiation.
+  auto softmax = [&](int t, const Ck& ck, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int j0 = t * BN;
+    const auto& c = ck.c;
     bool valid[2][16];
     if constexpr (MASKED) {
 #pragma unroll
@@ -403,12 +461,27 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         }
       mt = xhalf_max(mx);
     }
-    if constexpr (FP8) mt = ceilf(mt);
-    const bool grow = FP8 ? (mt > m) : (mt > m + 8.0f);
-    if (__any(grow)) {  // rare after the first tiles; O waits for the previous P.V here
-      const float mn = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float alpha;
+    if constexpr (FP8) {
+      // integer running maximum; the first finite one becomes the reference m0
+      mt = ceilf(mt);
+      if (m == -INFINITY) m0 = mt;
+      m = fmaxf(m, mt);
+      // O keeps the reference m0 unless m runs more than 100 past it; then O
+      // and l move to the new reference m0 = m.
+      const float mn0 = (m - m0 > 100.0f) ? m : m0;
+      alpha = mn0 == m0 ? 1.0f : __builtin_amdgcn_exp2f(m0 - mn0);
+      m0 = mn0;
+      pscale = 127 + (int)(m - m0);
+    } else {
+      // lazy running maximum: a row moves its reference m only when the tile
+      // maximum exceeds it by more than 8 (P <= 2^8 stays exact in fp16 and
+      // far from overflow)
+      const float mn = mt > m + 8.0f ? mt : m;
+      alpha = mn == m ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
+    }
+    if (__builtin_expect(__any(alpha != 1.0f), 0)) {
       lsum *= alpha;
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
@@ -431,73 +504,265 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
           pf[u][e] = hp[0];
           pf[u][e + 1] = hp[1];
         }
+      // P is complete here, in this (vector) phase: otherwise the compiler
+      // sinks the exponentials into the next matrix phase, next to their use
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v4i x = __builtin_bit_cast(v4i, pf[u]);
+        asm volatile("" : "+v"(x));
+        pf[u] = __builtin_bit_cast(v8h, x);
+      }
+      asm volatile("" : "+v"(lsum));
     } else {
+      float ps = 0.0f;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
           const float p0 = prob(jt, r), p1 = prob(jt, r + 1), p2 = prob(jt, r + 2), p3 = prob(jt, r + 3);
-          lsum += (p0 + p1) + (p2 + p3);
+          ps += (p0 + p1) + (p2 + p3);
           uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
           wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
           pf8[4 * jt + r / 4] = (int)wv;
         }
+      lsum += __builtin_ldexpf(ps, pscale - 127);
+      asm volatile("" : "+v"(pf8));
+      asm volatile("" : "+v"(lsum));
     }
   };
 
-  // prologue: tile 0 in stage 0 and its S; tile 1 in flight to stage 1
-  dma.issue(kseq, kn, vseq, vn, 0, L, lds, w);
+  // Ring slots: in phase b, kph = b % NSK and vph = b % NSV (advanced at the
+  // end of every phase); tile t lives in K slot t % NSK and V slot t % NSV.
+  int kph = 0, vph = 0;
+  auto wrapk = [](int x) { return x >= NSK ? x - NSK : x; };
+  auto wrapv = [](int x) { return x >= NSV ? x - NSV : x; };
+  auto koff = [](int slot) { return (uint32_t)(slot * S::KBYTES); };
+  auto voff = [](int slot) { return (uint32_t)(S::VRING + slot * S::VBYTES); };
+  // loads of tile t (fp16: K and V straight to LDS; FP8: K to LDS, V to registers)
+  // Descriptors of the next tile to load (every wave issues tiles 0, 1, 2, ...
+  // in order): base at the tile's first row, size up to the sequence's end.
+  const int8_t* knext = kseq;
+  const uint8_t* vnext = vseq;
+  int krec = (int)((L - 1) * kn + D), vrec = (int)((L - 1) * vn + 2 * D);
+  const int kstep = (int)(BN * kn), vstep = (int)(BN * vn);
+  auto issue = [&](int t, int ks, int vs) {
+    dma.issue_k(make_rsrc(knext, krec), lds + koff(ks), w);
+    knext += kstep;
+    krec -= kstep;
+    if constexpr (FP8) {
+      v8s.load(vseq, vn, t * BN, L, tid);
+    } else {
+      dma.issue_v(make_rsrc(vnext, vrec), lds + voff(vs), w);
+      vnext += vstep;
+      vrec -= vstep;
+    }
+  };
+  // Loads per wave per tile, fp16: the fewest any wave issues (waiting until
+  // that many are outstanding is never too little for anyone).
+  constexpr int LPT = (S::KCH >= NW ? S::KCH / NW : 0) + DmaPlan<D, FP8>::VPW;
+  static_assert(FP8 || (LPT >= 1 && LPT <= 3), "load count per tile");
+  auto wait_tile = [&](bool newer_in_flight) {  // this wave's loads of the older tile have landed
+    if (newer_in_flight) {
+      if constexpr (LPT == 1)
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      else if constexpr (LPT == 2)
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, tile 0 landed
   if constexpr (FP8) {
-    v8s.load(vseq, vn, 0, L, tid);
+    issue(0, 0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    v8s.store(lds + S::KBYTES, tid);
+    v8s.store(lds + voff(0), tid);
+    if (ntiles > 1) {
+      issue(1, 1, 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      v8s.store(lds + voff(1), tid);
+    }
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue(0, 0, 0);
+    if (ntiles > 1) issue(1, 1, 1);
+    wait_tile(ntiles > 1);
   }
   __syncthreads();
-  if (ntiles > 1) {
-    dma.issue(kseq, kn, vseq, vn, BN, L, lds + S::STAGE, w);
-    if constexpr (FP8) v8s.load(vseq, vn, BN, L, tid);
-  }
-  qk_tile<D>(lds + krow, kx_off, qf, magic, sc);
 
-  // Step t (stage t%3 holds tile t, (t+1)%3 tile t+1 in flight or landed):
-  // P.V of tile t-1 on the matrix cores while the VALU computes the softmax
-  // of tile t; then one barrier (tile t+1 has landed everywhere and every
-  // wave has finished reading stage (t-1)%3), the loads of tile t+2 into that
-  // stage, and the INT8 MFMAs of tile t+1 into sc.
-  for (int t = 0; t <= ntiles; ++t) {
-    if (t >= 1 && t - 1 < wtiles) pv(lds + ((t - 1) % 3) * S::STAGE);
-    if (t < wtiles) {
-      const int j0 = t * BN;
-      if ((j0 + BN > L) || (CAUSAL && j0 + BN - 1 > row0))
-        softmax(t, std::true_type{});
-      else
-        softmax(t, std::false_type{});
-    }
-    if (t + 1 < ntiles) {
-      lds_u8* nx1 = lds + ((t + 1) % 3) * S::STAGE;
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // own loads of tile t+1 landed, own V reads done
-      if constexpr (FP8) v8s.store(nx1 + S::KBYTES, tid);
-      __syncthreads();
-      if (t + 2 < ntiles) {
-        lds_u8* nx2 = lds + ((t + 2) % 3) * S::STAGE;
-        dma.issue(kseq, kn, vseq, vn, (t + 2) * BN, L, nx2, w);
-        if constexpr (FP8) v8s.load(vseq, vn, (t + 2) * BN, L, tid);
+  // ---- phases b = 0 .. ntiles+1, in pairs.  Matrix phase b: S of tile b and
+  // P.V of tile b-2; vector phase b: softmax of tile b-1.  Half 0 runs
+  // (matrix, vector) in each pair, half 1 (vector, matrix).  FULL pairs have
+  // every step valid and unmasked for this wave and run without checks.
+  const int nph = ntiles + 2;
+  auto begin_phase = [&](int b) {  // loads of tile b+2
+    if (b + 2 < ntiles) issue(b + 2, wrapk(kph + 2), wrapv(vph + 2));
+  };
+  auto end_phase = [&](int b) {
+    const bool more = b + 2 < ntiles;
+    if constexpr (FP8) {
+      if (more) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        v8s.store(lds + voff(wrapv(vph + 2)), tid);
       }
-      if (t + 1 < wtiles) qk_tile<D>(nx1 + krow, kx_off, qf, magic, sc);
-    }
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pfp[u] = pf[u];
     } else {
-      pf8p = pf8;
+      wait_tile(more);  // tile b+1 has landed (tile b+2 may still be in flight)
     }
+    // nothing moves across the phase boundary (the other half's work of the
+    // next phase must not start in this one)
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    kph = wrapk(kph + 1);
+    vph = wrapv(vph + 1);
+  };
+  // Matrix phase with every LDS operand read well ahead of its MFMA: all K
+  // fragments and the first V group, then the INT8 MFMAs, then per group of
+  // D/32 P.V MFMAs the V reads of the next group.
+  auto qk_pv = [&](uint32_t kso, uint32_t vso) {
+    v4i kf[2][D / 32];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) kf[jt][kk] = *(const LDS v4i*)(lds + kso + kofs[kk] + 32 * jt * D);
+    if constexpr (!FP8) {
+      uint32_t va[D / 32];
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct) va[ct] = vso + vaddr[ct];
+      v8h vf[4][D / 32];
+      auto vread = [&](int u) {
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct) {
+          const lds_u8* pa = lds + va[ct] + 16 * u * S::VROW;
+          const v4h ha = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)pa));
+          const v4h hb = __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)(pa + 8 * S::VROW)));
+          vf[u][ct] = __builtin_shufflevector(ha, hb, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      vread(0);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
+        sc[jt] = acc;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) vread(u + 1);
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u][ct], pf[u], o[ct], 0, 0, 0);
+      }
+      // order: K reads and V group 0; INT8 MFMAs; (V reads of group u+1, P.V MFMAs of group u) x 3; last group
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
+    } else {
+      const lds_u8* vl = lds + (vso + vrow8);  // V^T rows = channels
+      v8i vf[D / 32];
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct) {
+        const lds_u8* pa = vl + 32 * ct * S::VROW;
+        const v4i va = *(const LDS v4i*)(pa);
+        const v4i vb2 = *(const LDS v4i*)(pa + 16);
+        vf[ct] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
+        sc[jt] = acc;
+      }
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct)
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[ct], pf8, o[ct], 0, 0, 0, 127, 0, pscale);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3 * (D / 32), 0);
+    }
+  };
+  auto mphase = [&](int b, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    begin_phase(b);
+    if (FULL) {
+      qk_pv(koff(kph), voff(wrapv(vph + 3)));
+    } else {
+      if (b >= 2 && b - 2 < wtiles) pv(voff(wrapv(vph + 3)));
+      if (b < wtiles) qk_tile<D>(lds + koff(kph), kofs, qf, magic, sc);
+    }
+    end_phase(b);
+  };
+  auto vphase = [&](int b, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int t = b - 1;
+    const Ck ck = load_ck(min(max(t, 0), ntiles - 1));  // (t outside the tiles: value unused)
+    if (FULL) {
+      softmax(t, ck, std::false_type{});
+    } else if (t >= 0 && t < wtiles) {
+      const bool masked = (t * BN + BN > L) || (CAUSAL && t * BN + BN - 1 > row0);
+      if (masked)
+        softmax(t, ck, std::true_type{});
+      else
+        softmax(t, ck, std::false_type{});
+    }
+    begin_phase(b);  // after the softmax: its k_scale loads then wait for nothing newer
+    end_phase(b);
+  };
+  // tiles every key of which this wave sees (unmasked)
+  const int tu = CAUSAL ? min(L / BN, (row0 + 1) / BN) : L / BN;
+  auto run = [&](auto hf_tag) {
+    constexpr int HF = decltype(hf_tag)::value;
+    // FULL pair b0 (even): half 0: S(b0), P.V(b0-2), softmax(b0);
+    //                      half 1: softmax(b0-1), P.V(b0-1), S(b0+1)
+    const int bend = HF == 0 ? tu : min(tu + 1, wtiles - 1);
+    auto pair = [&](int b0, auto full_tag) {
+      if constexpr (HF == 0) {
+        mphase(b0, full_tag);
+        vphase(b0 + 1, full_tag);
+      } else {
+        vphase(b0, full_tag);
+        mphase(b0 + 1, full_tag);
+      }
+    };
+    pair(0, std::false_type{});
+    int b0 = 2;
+    for (; b0 < bend; b0 += 2) pair(b0, std::true_type{});
+    for (; b0 < nph; b0 += 2) pair(b0, std::false_type{});
+  };
+  if (hf == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+
+  // ---- merge the halves: half 1 leaves (O^T, m_ref, l) in LDS, half 0 combines.
+  // m_ref is the exponent O and l are relative to (fp16: m; FP8: m0), -inf
+  // if this half saw no key of the row.
+  float* const mg = (float*)lds + (w & 3) * S::MSTRIDE * 64 + lane;
+  const float mref_own = m == -INFINITY ? -INFINITY : (FP8 ? m0 : m);
+  if (hf == 1) {
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mg[(16 * ct + r) * 64] = o[ct][r];
+    mg[(D / 2) * 64] = mref_own;
+    mg[(D / 2 + 1) * 64] = lsum;
   }
+  __syncthreads();
+  if (hf == 1) return;
+  const float mref_b = mg[(D / 2) * 64], lsum_b = mg[(D / 2 + 1) * 64];
+  const float mmax = fmaxf(mref_own, mref_b);
+  const float wa = mref_own == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref_own - mmax);
+  const float wb = mref_b == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref_b - mmax);
 
   // ---- epilogue: O = O^T / l (FP8: l and O both carry the factor 448; times v_scale)
   _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h);
-  const float inv = 1.0f / xhalf_sum(lsum);
+  const float inv = 1.0f / xhalf_sum(lsum * wa + lsum_b * wb);
   if (i < L) {
     _Float16* orow = obase + (int64_t)i * a.os.n;
 #pragma unroll
@@ -508,7 +773,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         float f[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          f[e] = o[ct][4 * q + e] * inv;
+          const int r = 4 * q + e;
+          f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
           if constexpr (FP8) f[e] *= a.v_scale[sh * D + cc + e];
         }
         const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
@@ -519,21 +785,21 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 
 template <int D, bool FP8, bool CAUSAL, bool KSU>
 __global__ __launch_bounds__(NT) void k_attn(Problem p, AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[Lds<D, FP8>::NSTAGE * Lds<D, FP8>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[Lds<D, FP8>::BYTES];
   attn_body<D, FP8, CAUSAL, KSU>(p, a, (lds_u8*)lds_raw);
 }
 
 // Debug: the INT32 scores of the same staging (DmaPlan) and MFMA path
 // (qk_tile), before any dequantisation.  Dense problems, every query row and
-// key written.
+// key written; 8 waves x 32 rows per workgroup.
 template <int D>
 __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
-  using S = Lds<D, true>;  // K part only (the FP8 plan has no V DMA)
+  using S = Lds<D, true>;  // K part only
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::KBYTES];
   lds_u8* const lds = (lds_u8*)lds_raw;
   const int qt = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int L = seq_len(p.cu, s, p.max_seqlen);
-  const int q0 = qt * BM;
+  const int q0 = qt * NW * 32;
   if (q0 >= L) return;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -548,19 +814,19 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
-  int kx_off[D / 32];
+  uint32_t kofs[D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kx_off[kk] = 16 * ((2 * kk + g) ^ S::kswz(li));
+  for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * D + 16 * ((2 * kk + g) ^ S::kswz(li));
   for (int x = tid; x < S::KBYTES / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
   DmaPlan<D, true> dma;
   dma.init(w, lane, a.k8s.n, 0);
   for (int j0 = 0; j0 < L; j0 += BN) {
     __syncthreads();  // everyone is done reading the previous tile
-    dma.issue(kseq, a.k8s.n, nullptr, 0, j0, L, lds, w);
+    dma.issue_k(make_rsrc(kseq + (int64_t)j0 * a.k8s.n, (int)((L - 1 - j0) * a.k8s.n + D)), lds, w);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     v16i sc[2];
-    qk_tile<D>(lds + li * D, kx_off, qf, magic, sc);
+    qk_tile<D>(lds, kofs, qf, magic, sc);
     if (i < L) {
       int32_t* drow = a.dump + (sh * p.max_seqlen + i) * p.max_seqlen;
 #pragma unroll
@@ -595,7 +861,7 @@ hipError_t launch_ks(const Problem& p, const AttnArgs& a, hipStream_t st) {
 template <int D>
 hipError_t launch_d(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
   if (a.dump) {
-    const int nqt = (p.max_seqlen + BM - 1) / BM;
+    const int nqt = (p.max_seqlen + NW * 32 - 1) / (NW * 32);
     hipLaunchKernelGGL((k_qk_dump<D>), dim3(nqt, p.heads, p.nseq), dim3(NT), 0, st, p, a);
     return hipGetLastError();
   }
