@@ -147,27 +147,30 @@ __device__ __forceinline__ void dma_b128(const v4i& rsrc, int voff, uint32_t lds
 }
 __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
 
-// Per-lane constants of the direct-to-LDS tile loads.  Wave w fills the 1 KiB
-// blocks w, w+NW, ... of a tile; lane l lands at block + 16 l and fetches the
-// global 16-byte chunk the swizzle assigns there, at byte offset (row within
-// the tile) * row_stride + 16 * chunk.
+// Per-lane constants of the direct-to-LDS tile loads, issued by the 4 waves of
+// one half.  Wave w (0..3 within its half) fills the 1 KiB blocks w, w+4, ...
+// of a tile; lane l lands at block + 16 l and fetches the global 16-byte chunk
+// the swizzle assigns there, at byte offset (row within the tile) *
+// row_stride + 16 * chunk.
+constexpr int NWH = 4;  // waves per half
 template <int D, bool FP8>
 struct DmaPlan {
   using S = Lds<D, FP8>;
-  static constexpr int KPW = (S::KCH + NW - 1) / NW;  // K blocks per wave (some waves may have none)
-  static constexpr int VPW = S::VCH / NW;             // fp16 V blocks per wave
+  static constexpr int KPW = S::KCH / NWH;  // K blocks per wave
+  static constexpr int VPW = S::VCH / NWH;  // fp16 V blocks per wave
+  static_assert(S::KCH % NWH == 0 && S::VCH % NWH == 0, "tile blocks split over a half");
   int koff[KPW];
   int voff[VPW > 0 ? VPW : 1];
   __device__ void init(int w, int lane, int64_t kn, int64_t vn) {
 #pragma unroll
     for (int x = 0; x < KPW; ++x) {
-      const int byte = (w + NW * x) * 1024 + 16 * lane;
+      const int byte = (w + NWH * x) * 1024 + 16 * lane;
       const int r = byte / D, c = ((byte % D) / 16) ^ S::kswz(r);
       koff[x] = (int)(r * kn) + 16 * c;
     }
 #pragma unroll
     for (int x = 0; x < VPW; ++x) {
-      const int byte = (w + NW * x) * 1024 + 16 * lane;
+      const int byte = (w + NWH * x) * 1024 + 16 * lane;
       const int r = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ S::vswz(r);
       voff[x] = (int)(r * vn) + 16 * c;
     }
@@ -177,13 +180,12 @@ struct DmaPlan {
   // LDS bytes keep older, finite, data; those keys are masked).
   __device__ __forceinline__ void issue_k(const v4i& kr, lds_u8* slot, int w) const {
 #pragma unroll
-    for (int x = 0; x < KPW; ++x)
-      if (S::KCH % NW == 0 || w + NW * x < S::KCH) dma_b128(kr, koff[x], lds_addr(slot + (w + NW * x) * 1024));
+    for (int x = 0; x < KPW; ++x) dma_b128(kr, koff[x], lds_addr(slot + (w + NWH * x) * 1024));
   }
   __device__ __forceinline__ void issue_v(const v4i& vr, lds_u8* slot, int w) const {
     if constexpr (VPW > 0) {
 #pragma unroll
-      for (int x = 0; x < VPW; ++x) dma_b128(vr, voff[x], lds_addr(slot + (w + NW * x) * 1024));
+      for (int x = 0; x < VPW; ++x) dma_b128(vr, voff[x], lds_addr(slot + (w + NWH * x) * 1024));
     }
   }
 };
@@ -192,20 +194,21 @@ struct DmaPlan {
 // transposed.  Rows past the sequence are clamped to its last row.
 template <int D>
 struct V8Stager {
+  static constexpr int NTH = NWH * 64;  // threads of one half
   static constexpr int VITEMS = (BN / 4) * (D / 8);
-  static constexpr int VPT = (VITEMS + NT - 1) / NT;
+  static constexpr int VPT = (VITEMS + NTH - 1) / NTH;
   uint2 v8[VPT * 4];
   __device__ __forceinline__ void load(const uint8_t* vseq, int64_t vn, int j0, int L, int tid) {
     const __amdgpu_buffer_rsrc_t vr =
         __builtin_amdgcn_make_buffer_rsrc((void*)vseq, 0, (int)((L - 1) * vn + D), kRsrcWord3);
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int idx = tid + x * NT;
+      const int idx = tid + x * NTH;
       const int kq = idx % (BN / 4), cg = idx / (BN / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = min(j0 + 4 * kq + e, L - 1);
-        if (VITEMS % NT == 0 || idx < VITEMS)
+        if (VITEMS % NTH == 0 || idx < VITEMS)
           v8[x * 4 + e] =
               __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, (int)(row * vn) + 8 * cg, 0, 0));
       }
@@ -215,9 +218,9 @@ struct V8Stager {
     constexpr int VROW = Lds<D, true>::VROW;
 #pragma unroll
     for (int x = 0; x < VPT; ++x) {
-      const int idx = tid + x * NT;
+      const int idx = tid + x * NTH;
       const int kq = idx % (BN / 4), cg = idx / (BN / 4);
-      if (VITEMS % NT == 0 || idx < VITEMS) {
+      if (VITEMS % NTH == 0 || idx < VITEMS) {
         const int pos = pos8(kq);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -340,7 +343,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   __syncthreads();
 
   DmaPlan<D, FP8> dma;
-  dma.init(w, lane, kn, vn);
+  dma.init(w & 3, lane, kn, vn);  // the plan covers a tile with the 4 waves of one half
   V8Stager<D> v8s;
 
   float m = -INFINITY, lsum = 0.0f;
@@ -538,76 +541,49 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   auto wrapv = [](int x) { return x >= NSV ? x - NSV : x; };
   auto koff = [](int slot) { return (uint32_t)(slot * S::KBYTES); };
   auto voff = [](int slot) { return (uint32_t)(S::VRING + slot * S::VBYTES); };
-  // loads of tile t (fp16: K and V straight to LDS; FP8: K to LDS, V to registers)
-  // Descriptors of the next tile to load (every wave issues tiles 0, 1, 2, ...
-  // in order): base at the tile's first row, size up to the sequence's end.
-  const int8_t* knext = kseq;
-  const uint8_t* vnext = vseq;
-  int krec = (int)((L - 1) * kn + D), vrec = (int)((L - 1) * vn + 2 * D);
-  const int kstep = (int)(BN * kn), vstep = (int)(BN * vn);
+  // Tile loads.  The half that owns tile t (t = hf mod 2) loads it, in its
+  // matrix phase t-2, and waits for it at the end of its vector phase t-1;
+  // the barrier after that publishes it for the matrix phase t (K) and t+2
+  // (V), both run by the same half.  fp16: K and V straight to LDS; FP8: K to
+  // LDS, V to registers (stored transposed at the end of phase t-1).
+  // Descriptors of this half's next tile: base at the tile's first row, size
+  // up to the sequence's end.
+  const int8_t* knext = kseq + (int64_t)hf * BN * kn;
+  const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
+  int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + 2 * D);
+  const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
+  const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
   auto issue = [&](int t, int ks, int vs) {
-    dma.issue_k(make_rsrc(knext, krec), lds + koff(ks), w);
+    dma.issue_k(make_rsrc(knext, krec), lds + koff(ks), wh);
     knext += kstep;
     krec -= kstep;
     if constexpr (FP8) {
-      v8s.load(vseq, vn, t * BN, L, tid);
+      v8s.load(vseq, vn, t * BN, L, tidh);
     } else {
-      dma.issue_v(make_rsrc(vnext, vrec), lds + voff(vs), w);
+      dma.issue_v(make_rsrc(vnext, vrec), lds + voff(vs), wh);
       vnext += vstep;
       vrec -= vstep;
     }
   };
-  // Loads per wave per tile, fp16: the fewest any wave issues (waiting until
-  // that many are outstanding is never too little for anyone).
-  constexpr int LPT = (S::KCH >= NW ? S::KCH / NW : 0) + DmaPlan<D, FP8>::VPW;
-  static_assert(FP8 || (LPT >= 1 && LPT <= 3), "load count per tile");
-  auto wait_tile = [&](bool newer_in_flight) {  // this wave's loads of the older tile have landed
-    if (newer_in_flight) {
-      if constexpr (LPT == 1)
-        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-      else if constexpr (LPT == 2)
-        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-  };
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 landed
-  if constexpr (FP8) {
-    issue(0, 0, 0);
+  // ---- prologue: half h loads tile h
+  if (hf < ntiles) {
+    issue(hf, hf, hf);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    v8s.store(lds + voff(0), tid);
-    if (ntiles > 1) {
-      issue(1, 1, 1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      v8s.store(lds + voff(1), tid);
-    }
-  } else {
-    issue(0, 0, 0);
-    if (ntiles > 1) issue(1, 1, 1);
-    wait_tile(ntiles > 1);
+    if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
   }
   __syncthreads();
 
   // ---- phases b = 0 .. ntiles+1, in pairs.  Matrix phase b: S of tile b and
-  // P.V of tile b-2; vector phase b: softmax of tile b-1.  Half 0 runs
-  // (matrix, vector) in each pair, half 1 (vector, matrix).  FULL pairs have
-  // every step valid and unmasked for this wave and run without checks.
+  // P.V of tile b-2, and the loads of tile b+2; vector phase b: softmax of
+  // tile b-1, then wait for tile b+1.  Half 0 runs (matrix, vector) in each
+  // pair, half 1 (vector, matrix).  FULL pairs have every step valid and
+  // unmasked for this wave and run without checks.
   const int nph = ntiles + 2;
-  auto begin_phase = [&](int b) {  // loads of tile b+2
-    if (b + 2 < ntiles) issue(b + 2, wrapk(kph + 2), wrapv(vph + 2));
-  };
-  auto end_phase = [&](int b) {
-    const bool more = b + 2 < ntiles;
-    if constexpr (FP8) {
-      if (more) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        v8s.store(lds + voff(wrapv(vph + 2)), tid);
-      }
-    } else {
-      wait_tile(more);  // tile b+1 has landed (tile b+2 may still be in flight)
+  auto end_phase = [&](int b, bool vector_phase) {
+    if (vector_phase && b + 1 < ntiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this half's loads of tile b+1
+      if constexpr (FP8) v8s.store(lds + voff(wrapv(vph + 1)), tidh);
     }
     // nothing moves across the phase boundary (the other half's work of the
     // next phase must not start in this one)
@@ -618,9 +594,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     vph = wrapv(vph + 1);
   };
   // Matrix phase with every LDS operand read well ahead of its MFMA: all K
-  // fragments and the first V group, then the INT8 MFMAs, then per group of
-  // D/32 P.V MFMAs the V reads of the next group.
-  auto qk_pv = [&](uint32_t kso, uint32_t vso) {
+  // fragments and the first V group, then (while those reads are in flight)
+  // mid() -- the tile loads --, the INT8 MFMAs, then per group of D/32 P.V
+  // MFMAs the V reads of the next group.
+  auto qk_pv = [&](uint32_t kso, uint32_t vso, auto&& mid) {
     v4i kf[2][D / 32];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
@@ -641,6 +618,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         }
       };
       vread(0);
+      mid();
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
@@ -654,8 +632,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u][ct], pf[u], o[ct], 0, 0, 0);
       }
-      // order: K reads and V group 0; INT8 MFMAs; (V reads of group u+1, P.V MFMAs of group u) x 3; last group
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
+      // order after mid(): INT8 MFMAs; (V reads of group u+1, P.V MFMAs of group u) x 3; last group
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
@@ -673,6 +650,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         const v4i vb2 = *(const LDS v4i*)(pa + 16);
         vf[ct] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
       }
+      mid();
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
@@ -683,20 +661,21 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct)
         o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[ct], pf8, o[ct], 0, 0, 0, 127, 0, pscale);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * (D / 32), 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 3 * (D / 32), 0);
     }
   };
   auto mphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    begin_phase(b);
+    auto loads = [&] {  // tile b+2 (owned by this half)
+      if (b + 2 < ntiles) issue(b + 2, wrapk(kph + 2), wrapv(vph + 2));
+    };
     if (FULL) {
-      qk_pv(koff(kph), voff(wrapv(vph + 3)));
+      qk_pv(koff(kph), voff(wrapv(vph + 3)), loads);
     } else {
+      loads();
       if (b >= 2 && b - 2 < wtiles) pv(voff(wrapv(vph + 3)));
       if (b < wtiles) qk_tile<D>(lds + koff(kph), kofs, qf, magic, sc);
     }
-    end_phase(b);
+    end_phase(b, false);
   };
   auto vphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -711,8 +690,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       else
         softmax(t, ck, std::false_type{});
     }
-    begin_phase(b);  // after the softmax: its k_scale loads then wait for nothing newer
-    end_phase(b);
+    end_phase(b, true);
   };
   // tiles every key of which this wave sees (unmasked)
   const int tu = CAUSAL ? min(L / BN, (row0 + 1) / BN) : L / BN;
@@ -819,10 +797,11 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
   for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * D + 16 * ((2 * kk + g) ^ S::kswz(li));
   for (int x = tid; x < S::KBYTES / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
   DmaPlan<D, true> dma;
-  dma.init(w, lane, a.k8s.n, 0);
+  dma.init(w & 3, lane, a.k8s.n, 0);
   for (int j0 = 0; j0 < L; j0 += BN) {
     __syncthreads();  // everyone is done reading the previous tile
-    dma.issue_k(make_rsrc(kseq + (int64_t)j0 * a.k8s.n, (int)((L - 1 - j0) * a.k8s.n + D)), lds, w);
+    if (w < NWH)  // the plan covers a tile with 4 waves
+      dma.issue_k(make_rsrc(kseq + (int64_t)j0 * a.k8s.n, (int)((L - 1 - j0) * a.k8s.n + D)), lds, w);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     v16i sc[2];
