@@ -42,11 +42,12 @@
 // its matrix phase: INT8 S of tile b and the P.V of tile b-2; the other half
 // is in its vector phase: the softmax of tile b-1.  So at any time one wave
 // of every SIMD feeds the matrix core while the other keeps the VALU busy,
-// and S and P need one register set each.  At the start of phase b every
-// wave issues its share of the loads of tile b+2 (K straight into LDS with
-// buffer_load ... lds; fp16 V too, E4M3 V through registers so it can be
-// transposed).  K tiles live in a ring of 3 LDS slots (read in phase t), V
-// tiles in a ring of 5 (read in phase t+2).
+// and S and P need one register set each.  The half in its matrix phase b
+// also issues the loads of the tiles it will use next: V(b+2) and K(b+4) (K
+// straight into LDS with buffer_load ... lds; fp16 V too, E4M3 V through
+// registers so it can be transposed), and waits for them at the end of its
+// vector phase b+3, ~3.5 phases later.  K and V tiles live in rings of 5 LDS
+// slots.
 //
 // Softmax.  The i32 accumulator starts at the bit pattern of 1.5*2^23, so the
 // MFMA leaves the float 1.5*2^23 + S exactly (|S| <= 127^2*128 < 2^22): no
@@ -86,7 +87,7 @@ constexpr int BN = 64;                  // keys per tile
 constexpr int NW = 8;                   // waves per workgroup (two halves of 4)
 constexpr int NT = NW * 64;
 constexpr int BM = 128;                 // query rows per workgroup (32 per wave of a half)
-constexpr int NSK = 3;                  // K ring slots
+constexpr int NSK = 5;                  // K ring slots
 constexpr int NSV = 5;                  // V ring slots
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9 (raw, 32-bit format)
 
@@ -181,6 +182,12 @@ struct DmaPlan {
   __device__ __forceinline__ void issue_k(const v4i& kr, lds_u8* slot, int w) const {
 #pragma unroll
     for (int x = 0; x < KPW; ++x) dma_b128(kr, koff[x], lds_addr(slot + (w + NWH * x) * 1024));
+  }
+  __device__ __forceinline__ void issue_k1(const v4i& kr, lds_u8* slot, int w, int x) const {
+    dma_b128(kr, koff[x], lds_addr(slot + (w + NWH * x) * 1024));
+  }
+  __device__ __forceinline__ void issue_v1(const v4i& vr, lds_u8* slot, int w, int x) const {
+    if constexpr (VPW > 0) dma_b128(vr, voff[x], lds_addr(slot + (w + NWH * x) * 1024));
   }
   __device__ __forceinline__ void issue_v(const v4i& vr, lds_u8* slot, int w) const {
     if constexpr (VPW > 0) {
@@ -446,9 +453,17 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         if constexpr (MASKED) return valid[jt][r] ? xx : 0.0f;
         return xx;
       };
-      float mx = fmaxf(xv(0, 0), xv(0, 1));
+      // four independent max3 chains (one wave does all the VALU work of a
+      // phase, so a single chain would leave the VALU waiting on its latency)
+      float mc[4];
 #pragma unroll
-      for (int r = 2; r < 32; r += 2) mx = fmaxf(fmaxf(mx, xv(r >> 4, r & 15)), xv((r + 1) >> 4, (r + 1) & 15));
+      for (int c4 = 0; c4 < 4; ++c4) mc[c4] = fmaxf(xv(c4 >> 1, 8 * (c4 & 1)), xv(c4 >> 1, 8 * (c4 & 1) + 1));
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int r = 2; r < 8; r += 2)
+          mc[c4] = fmaxf(fmaxf(mc[c4], xv(c4 >> 1, 8 * (c4 & 1) + r)), xv(c4 >> 1, 8 * (c4 & 1) + r + 1));
+      float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
       mx = xhalf_max(mx);
       // every real x is >= 1.5*2^23 - 2^21 > 0, so 0 means "all masked": leave m alone
       mt = (MASKED && mx == 0.0f) ? -INFINITY : (mx - kMagic) * c[0][0];
@@ -498,15 +513,17 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     };
     if constexpr (!FP8) {
       const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+      float ls[2] = {lsum, 0.0f};  // two independent accumulation chains
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const v2h hp = {(_Float16)prob(u >> 1, 8 * (u & 1) + e), (_Float16)prob(u >> 1, 8 * (u & 1) + e + 1)};
-          lsum = __builtin_amdgcn_fdot2(hp, ones, lsum, false);
+          ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2(hp, ones, ls[(e >> 1) & 1], false);
           pf[u][e] = hp[0];
           pf[u][e + 1] = hp[1];
         }
+      lsum = ls[0] + ls[1];
       // P is complete here, in this (vector) phase: otherwise the compiler
       // sinks the exponentials into the next matrix phase, next to their use
 #pragma unroll
@@ -534,75 +551,110 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     }
   };
 
-  // Ring slots: in phase b, kph = b % NSK and vph = b % NSV (advanced at the
-  // end of every phase); tile t lives in K slot t % NSK and V slot t % NSV.
-  int kph = 0, vph = 0;
-  auto wrapk = [](int x) { return x >= NSK ? x - NSK : x; };
-  auto wrapv = [](int x) { return x >= NSV ? x - NSV : x; };
+  // Ring slots: tile t lives in K slot t % NSK and V slot t % NSV (NSK = NSV =
+  // 5); ph = b % 5 is advanced at the end of every phase.
+  static_assert(NSK == 5 && NSV == 5, "slot arithmetic below");
+  int ph = 0;
+  auto wrap = [](int x) { return x >= 5 ? x - 5 : x; };
   auto koff = [](int slot) { return (uint32_t)(slot * S::KBYTES); };
   auto voff = [](int slot) { return (uint32_t)(S::VRING + slot * S::VBYTES); };
-  // Tile loads.  The half that owns tile t (t = hf mod 2) loads it, in its
-  // matrix phase t-2, and waits for it at the end of its vector phase t-1;
-  // the barrier after that publishes it for the matrix phase t (K) and t+2
-  // (V), both run by the same half.  fp16: K and V straight to LDS; FP8: K to
-  // LDS, V to registers (stored transposed at the end of phase t-1).
-  // Descriptors of this half's next tile: base at the tile's first row, size
-  // up to the sequence's end.
+  // Tile loads.  The half that owns tile t (t = hf mod 2) loads K(t) in its
+  // matrix phase t-4 and V(t) in its matrix phase t-2 (V is first read in
+  // phase t+2), and waits for both at the end of its vector phase t-1, with
+  // the loads of its matrix phase t-2 still in flight: ~3.5 phases of latency
+  // hidden.  The barrier after that publishes them for the matrix phases t
+  // (K) and t+2 (V), run by the same half.  fp16: K and V straight to LDS;
+  // FP8: K to LDS, V to registers, stored transposed at the end of phase t-1.
+  // Descriptors of this half's next K and V tiles: base at the tile's first
+  // row, size up to the sequence's end.
   const int8_t* knext = kseq + (int64_t)hf * BN * kn;
   const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
   int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + 2 * D);
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
-  auto issue = [&](int t, int ks, int vs) {
-    dma.issue_k(make_rsrc(knext, krec), lds + koff(ks), wh);
-    knext += kstep;
-    krec -= kstep;
-    if constexpr (FP8) {
-      v8s.load(vseq, vn, t * BN, L, tidh);
-    } else {
-      dma.issue_v(make_rsrc(vnext, vrec), lds + voff(vs), wh);
-      vnext += vstep;
-      vrec -= vstep;
-    }
+  constexpr int KL = DmaPlan<D, FP8>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8>::VPW;
+  constexpr int NOPS = KL + VL;  // DMA loads per wave per matrix phase
+  // Every matrix phase issues NOPS DMA loads per wave (fp16: VL for V, then KL
+  // for K; FP8: its V loads to registers come first, then the KL K loads).  At
+  // the end of a vector phase the loads of the previous matrix phase may stay
+  // in flight: s_waitcnt vmcnt(NOPS) (FP8: vmcnt(KL), its V registers are
+  // needed now).
+  auto wait_older = [&] {
+    constexpr int n = FP8 ? KL : NOPS;
+    static_assert(n >= 1 && n <= 6, "wait counts below");
+    if constexpr (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   };
 
-  // ---- prologue: half h loads tile h
-  if (hf < ntiles) {
-    issue(hf, hf, hf);
+  // ---- prologue: half h loads K(h), K(h+2) and V(h) (empty descriptors past the end)
+  {
+    if constexpr (FP8)
+      v8s.load(vseq, vn, hf * BN, L, tidh);
+    else
+      dma.issue_v(make_rsrc(vnext, max(vrec, 0)), lds + voff(hf), wh);
+    vnext += vstep;
+    vrec -= vstep;
+    dma.issue_k(make_rsrc(knext, max(krec, 0)), lds + koff(hf), wh);
+    dma.issue_k(make_rsrc(knext + kstep, max(krec - kstep, 0)), lds + koff(hf + 2), wh);
+    knext += 2 * kstep;
+    krec -= 2 * kstep;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
   }
+  // The compiler's own bookkeeping of outstanding loads (Q, the k_scale
+  // table) ends here: it must not add waits for them inside the loop, where
+  // they would also wait for the tile loads it does not see.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   // ---- phases b = 0 .. ntiles+1, in pairs.  Matrix phase b: S of tile b and
-  // P.V of tile b-2, and the loads of tile b+2; vector phase b: softmax of
-  // tile b-1, then wait for tile b+1.  Half 0 runs (matrix, vector) in each
-  // pair, half 1 (vector, matrix).  FULL pairs have every step valid and
+  // P.V of tile b-2, and the loads V(b+2), K(b+4); vector phase b: softmax of
+  // tile b-1, then wait for K(b+1), V(b-1).  Half 0 runs (matrix, vector) in
+  // each pair, half 1 (vector, matrix).  FULL pairs have every step valid and
   // unmasked for this wave and run without checks.
   const int nph = ntiles + 2;
   auto end_phase = [&](int b, bool vector_phase) {
-    if (vector_phase && b + 1 < ntiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this half's loads of tile b+1
-      if constexpr (FP8) v8s.store(lds + voff(wrapv(vph + 1)), tidh);
+    if (vector_phase) {
+      // K(b+1) and V(b-1) must have landed; in flight from matrix phase b-1
+      // may stay: V(b+1), then K(b+3)
+      wait_older();
+      if constexpr (FP8) v8s.store(lds + voff(wrap(ph + 1)), tidh);  // V(b+1), from registers
     }
     // nothing moves across the phase boundary (the other half's work of the
     // next phase must not start in this one)
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    kph = wrapk(kph + 1);
-    vph = wrapv(vph + 1);
+    ph = wrap(ph + 1);
   };
   // Matrix phase with every LDS operand read well ahead of its MFMA: all K
-  // fragments and the first V group, then (while those reads are in flight)
-  // mid() -- the tile loads --, the INT8 MFMAs, then per group of D/32 P.V
-  // MFMAs the V reads of the next group.
-  auto qk_pv = [&](uint32_t kso, uint32_t vso, auto&& mid) {
+  // fragments and the first V group; then the INT8 MFMAs with this phase's
+  // tile loads (op(0) .. op(NOPS-1)) issued one per MFMA, in their shadow;
+  // then per group of D/32 P.V MFMAs the V reads of the next group.
+  auto qk_pv = [&](uint32_t kso, uint32_t vso, auto&& op) {
     v4i kf[2][D / 32];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) kf[jt][kk] = *(const LDS v4i*)(lds + kso + kofs[kk] + 32 * jt * D);
+    // (sched_barrier(0): the instruction order below is the schedule)
+    auto qk_mfmas = [&] {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        v16i acc = magic;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
+          if (jt * (D / 32) + kk < NOPS) op(jt * (D / 32) + kk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sc[jt] = acc;
+      }
+    };
     if constexpr (!FP8) {
       uint32_t va[D / 32];
 #pragma unroll
@@ -618,28 +670,15 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         }
       };
       vread(0);
-      mid();
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
-#pragma unroll
-        for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
-        sc[jt] = acc;
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk_mfmas();
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u + 1 < 4) vread(u + 1);
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u][ct], pf[u], o[ct], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // order after mid(): INT8 MFMAs; (V reads of group u+1, P.V MFMAs of group u) x 3; last group
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 32), 0);
-#pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 32), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
     } else {
       const lds_u8* vl = lds + (vso + vrow8);  // V^T rows = channels
       v8i vf[D / 32];
@@ -650,14 +689,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         const v4i vb2 = *(const LDS v4i*)(pa + 16);
         vf[ct] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      mid();
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][0], qf[0], magic, 0, 0, 0);
-#pragma unroll
-        for (int kk = 1; kk < D / 32; ++kk) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
-        sc[jt] = acc;
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      qk_mfmas();
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct)
         o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[ct], pf8, o[ct], 0, 0, 0, 127, 0, pscale);
@@ -665,16 +698,32 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   };
   auto mphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    auto loads = [&] {  // tile b+2 (owned by this half)
-      if (b + 2 < ntiles) issue(b + 2, wrapk(kph + 2), wrapv(vph + 2));
+    // Loads V(b+2), then K(b+4), of tiles owned by this half, as NOPS single
+    // loads.  They are issued whether or not the tile exists (past the end
+    // the descriptor is empty: nothing is read, the slot written holds a
+    // consumed tile), so every matrix phase has the same count in flight.
+    const v4i vr = make_rsrc(vnext, max(vrec, 0)), kr = make_rsrc(knext, max(krec, 0));
+    lds_u8* const vsl = lds + voff(wrap(ph + 2));
+    lds_u8* const ksl = lds + koff(wrap(ph + 4));
+    if constexpr (FP8) v8s.load(vseq, vn, (b + 2) * BN, L, tidh);
+    auto op = [&](int x) {
+      if (x < VL)
+        dma.issue_v1(vr, vsl, wh, x);
+      else
+        dma.issue_k1(kr, ksl, wh, x - VL);
     };
     if (FULL) {
-      qk_pv(koff(kph), voff(wrapv(vph + 3)), loads);
+      qk_pv(koff(ph), voff(wrap(ph + 3)), op);
     } else {
-      loads();
-      if (b >= 2 && b - 2 < wtiles) pv(voff(wrapv(vph + 3)));
-      if (b < wtiles) qk_tile<D>(lds + koff(kph), kofs, qf, magic, sc);
+#pragma unroll
+      for (int x = 0; x < NOPS; ++x) op(x);
+      if (b >= 2 && b - 2 < wtiles) pv(voff(wrap(ph + 3)));
+      if (b < wtiles) qk_tile<D>(lds + koff(ph), kofs, qf, magic, sc);
     }
+    knext += kstep;
+    krec -= kstep;
+    vnext += vstep;
+    vrec -= vstep;
     end_phase(b, false);
   };
   auto vphase = [&](int b, auto full_tag) {
@@ -723,6 +772,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // if this half saw no key of the row.
   float* const mg = (float*)lds + (w & 3) * S::MSTRIDE * 64 + lane;
   const float mref_own = m == -INFINITY ? -INFINITY : (FP8 ? m0 : m);
+  // the last matrix phases' loads (past the last tile) are still in flight and
+  // write into the ring, which the partial results reuse
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   if (hf == 1) {
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
