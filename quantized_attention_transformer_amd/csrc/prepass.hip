@@ -11,9 +11,10 @@
 //
 // All of these are HBM-bound streaming passes.  Rounding is fixed so that the
 // results are bit-exact against a plain CPU implementation:
-//   * K column sums are taken in fp64; every fp16 value is a multiple of
-//     2^-24 and the sums stay far below 2^29, so each partial sum is exact
-//     and the result is independent of the reduction order.  mean =
+//   * K column sums are taken in fp64 (one partial per Q block, fused with
+//     the Q quantisation, then a small reduction); every fp16 value is a
+//     multiple of 2^-24 and the sums stay far below 2^29, so each partial sum
+//     is exact and the result is independent of the reduction order.  mean =
 //     fp32(sum / L) with one IEEE fp64 division.
 //   * Q' = fp32(Q * sm_scale), K' = fp32(K - mean): one rounding each.
 //   * scale = fp32(absmax / 127) and code = rint(fp32(x / scale)) use IEEE
@@ -55,94 +56,38 @@ __device__ __forceinline__ H8 load_h8(const _Float16* p) {
   return r;
 }
 
-// ---------------------------------------------------------------- K column sums
-// grid (nchunk, heads, nseq): fp64 sums of K over one chunk of tokens.
+// ---------------------------------------------------------------- INT8 blocks
+// Rows of a block of up to 128 rows held in registers: thread (r, cg) holds
+// rows n0 + r + RPP*j, j < R, channels 8cg .. 8cg+7.  All loads are issued
+// before any is used, so the block costs one memory round trip.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_colsum(const _Float16* __restrict__ K, Str ks,
-                                                      const int32_t* __restrict__ cu, int max_seqlen,
-                                                      int nchunk, double* __restrict__ part) {
-  constexpr int TPR = D / 8, RPP = kThreads / TPR;
-  const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
-  const int n0 = chunk * kColChunk;
-  if (n0 >= L) return;
-  const int n1 = min(L, n0 + kColChunk);
-  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
-  const _Float16* base = K + seq_head_base(cu, ks, s, h) + cg * 8;
-  double acc[8] = {};
-#pragma unroll 4
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(base + (int64_t)n * ks.n);
+struct BlockRows {
+  static constexpr int TPR = D / 8, RPP = kThreads / TPR, R = 128 / RPP;
+  H8 x[R];
+  __device__ __forceinline__ void load(const _Float16* __restrict__ src, int64_t sn, int n0, int n1) {
+    const int r = threadIdx.x / TPR;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+    for (int j = 0; j < R; ++j) {
+      const int n = n0 + r + RPP * j;
+      if (n < n1) x[j] = load_h8(src + (int64_t)n * sn);
+    }
   }
-  __shared__ double red[RPP][D];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = acc[i];
-  __syncthreads();
-  if (tid < D) {
-    double t = 0.0;
-    for (int i = 0; i < RPP; ++i) t += red[i][tid];
-    part[(((int64_t)s * H + h) * nchunk + chunk) * D + tid] = t;
-  }
-}
+};
 
-// grid (heads, nseq), D threads: mean = fp32(sum / L).
-__global__ void k_mean_finalize(const double* __restrict__ part, const int32_t* __restrict__ cu, int max_seqlen,
-                       int nchunk, float* __restrict__ km) {
-  const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, D = blockDim.x, c = threadIdx.x;
-  const int L = seq_len(cu, s, max_seqlen);
-  const int nc = (L + kColChunk - 1) / kColChunk;
-  double t = 0.0;
-  for (int k = 0; k < nc; ++k) t += part[(((int64_t)s * H + h) * nchunk + k) * D + c];
-  km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(t / (double)L) : 0.0f;
-}
-
-// ---------------------------------------------------------------- INT8 Q / K
-// grid (nbq + nbk, heads, nseq): one quantisation block of Q (x < nbq) or K.
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_quant_qk(
-    const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks,
-    const int32_t* __restrict__ cu, int max_seqlen, int blk_q, int blk_k, int nbq, int nbk, float sm_scale,
-    const float* __restrict__ km, int8_t* __restrict__ q8, Str q8s, int8_t* __restrict__ k8, Str k8s,
-    float* __restrict__ sq, float* __restrict__ sk) {
-  constexpr int TPR = D / 8, RPP = kThreads / TPR;
-  const int b = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const bool isq = b < nbq;
-  const int blk = isq ? blk_q : blk_k;
-  const int bi = isq ? b : b - nbq;
-  const int L = seq_len(cu, s, max_seqlen);
-  const int n0 = bi * blk;
-  if (n0 >= L) return;
-  const int n1 = min(L, n0 + blk);
-  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
-  const Str xs = isq ? qs : ks;
-  const _Float16* src = (isq ? Q : K) + seq_head_base(cu, xs, s, h) + cg * 8;
-  float mean[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) mean[i] = isq ? 0.0f : km[((int64_t)s * H + h) * D + cg * 8 + i];
-
-  auto transform = [&](float v, int i) -> float {
-    // one fp32 rounding: Q * sm_scale, or K - mean(K)
-    return isq ? v * sm_scale : v - mean[i];
-  };
-
-  float amax = 0.0f;
-#pragma unroll 2
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(src + (int64_t)n * xs.n);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x.v[i], i)));
-  }
-  const float a = block_max(amax);
-  const float scale = a > 0.0f ? a / 127.0f : 0.0f;
-  if (tid == 0) (isq ? sq : sk)[((int64_t)s * H + h) * (isq ? nbq : nbk) + bi] = scale;
-
-  const Str ds = isq ? q8s : k8s;
-  int8_t* dst = (isq ? q8 : k8) + seq_head_base(cu, ds, s, h) + cg * 8;
-#pragma unroll 2
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(src + (int64_t)n * xs.n);
+// One quantisation block, rows [n0, n1) of one (sequence, head): thread (r,
+// cg) handles rows n0 + r + RPP*j, channels 8cg .. 8cg+7 (16-byte loads).
+// x' = transform(x) (one fp32 rounding), scale = fp32(absmax / 127), code =
+// rint(x' / scale) clipped to +-127 (0 when the block is all zero).  Blocks
+// of up to 128 rows stay in registers between the absmax and the codes (one
+// read of HBM; `pre`: already loaded); longer ones are read twice.  Returns
+// the scale.
+template <int D, typename F>
+__device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, int64_t sn, int n0, int n1,
+                                             F transform, int8_t* __restrict__ dst, int64_t dn,
+                                             const BlockRows<D>* pre = nullptr) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR, R = 128 / RPP;
+  const int tid = threadIdx.x, r = tid / TPR;
+  auto codes = [&](const H8& x, float a, float scale) {
     uint32_t w[2] = {0u, 0u};
     if (a > 0.0f) {
 #pragma unroll
@@ -152,8 +97,174 @@ __global__ __launch_bounds__(kThreads) void k_quant_qk(
         w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (i & 3));
       }
     }
-    *reinterpret_cast<uint2*>(dst + (int64_t)n * ds.n) = make_uint2(w[0], w[1]);
+    return make_uint2(w[0], w[1]);
+  };
+  float amax = 0.0f;
+  if (n1 - n0 <= RPP * R) {
+    BlockRows<D> rows;
+    if (pre)
+      rows = *pre;
+    else
+      rows.load(src, sn, n0, n1);
+    const H8* x = rows.x;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (n0 + r + RPP * j < n1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x[j].v[i], i)));
+    const float a = block_max(amax);
+    const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int n = n0 + r + RPP * j;
+      if (n < n1) *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) = codes(x[j], a, scale);
+    }
+    return scale;
   }
+#pragma unroll 2
+  for (int n = n0 + r; n < n1; n += RPP) {
+    H8 x = load_h8(src + (int64_t)n * sn);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x.v[i], i)));
+  }
+  const float a = block_max(amax);
+  const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+#pragma unroll 2
+  for (int n = n0 + r; n < n1; n += RPP)
+    *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) = codes(load_h8(src + (int64_t)n * sn), a, scale);
+  return scale;
+}
+
+// grid (2*nbq, heads, nseq): workgroup 2bi quantises Q block bi (INT8 Q' = Q *
+// sm_scale); workgroup 2bi+1 takes the fp64 column sums of K over the same
+// rows, one partial per Q block.
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_quant_q_colsum(
+    const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
+    int max_seqlen, int blk_q, int nbq, float sm_scale, int8_t* __restrict__ q8, Str q8s, float* __restrict__ sq,
+    double* __restrict__ part) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int bi = blockIdx.x >> 1, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = bi * blk_q;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + blk_q);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const int64_t sh = (int64_t)s * H + h;
+  if ((blockIdx.x & 1) == 0) {
+    const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1,
+                                       [&](float v, int) { return v * sm_scale; },
+                                       q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n);
+    if (tid == 0) sq[sh * nbq + bi] = scale;
+    return;
+  }
+  // K column sums (exact in fp64, in any order)
+  const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
+  double acc[8] = {};
+  if (n1 - n0 <= 128) {
+    BlockRows<D> krows;
+    krows.load(kb, ks.n, n0, n1);
+#pragma unroll
+    for (int j = 0; j < BlockRows<D>::R; ++j)
+      if (n0 + r + RPP * j < n1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (double)(float)krows.x[j].v[i];
+  } else {
+#pragma unroll 4
+    for (int n = n0 + r; n < n1; n += RPP) {
+      H8 x = load_h8(kb + (int64_t)n * ks.n);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+    }
+  }
+  __shared__ double red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) t += red[i][tid];
+    part[(sh * nbq + bi) * D + tid] = t;
+  }
+}
+
+// Sum of the nb = ceil(L / blk_q) partials of channel c of (s, h), by the
+// kThreads / D threads of c (16 independent loads per round), combined in LDS.
+template <int D>
+__device__ __forceinline__ double sum_partials(const double* __restrict__ pp, int nb, int c, int g) {
+  constexpr int G = kThreads / D;
+  double tot = 0.0;
+  for (int k0 = g; k0 < nb; k0 += 16 * G) {
+    double t[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + u * G;
+      t[u] = k < nb ? pp[(int64_t)k * D] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) tot += t[u];
+  }
+  __shared__ double red[G][D];
+  red[g][c] = tot;
+  __syncthreads();
+  double sum = 0.0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) sum += red[i][c];
+  return sum;
+}
+
+// grid (heads, nseq), kThreads: mean = fp32(sum / L) from the per-Q-block
+// partials (long sequences; shorter ones fold this into k_quant_k).
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_mean_finalize(const double* __restrict__ part,
+                                                            const int32_t* __restrict__ cu, int max_seqlen, int blk_q,
+                                                            int nbq, float* __restrict__ km) {
+  const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int nb = (L + blk_q - 1) / blk_q;
+  const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nbq * D + c, nb, c, g);
+  if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(sum / (double)L) : 0.0f;
+}
+
+// grid (nbk, heads, nseq): K block bi -> INT8 K' = K - mean(K).  FOLD: the
+// workgroup sums the column partials itself (every block of the head does;
+// block 0 stores k_mean), otherwise k_mean comes from k_mean_finalize.
+template <int D, bool FOLD>
+__global__ __launch_bounds__(kThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
+                                                      const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
+                                                      int nbk, int blk_q, int nbq, const double* __restrict__ part,
+                                                      float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
+                                                      float* __restrict__ sk) {
+  constexpr int TPR = D / 8;
+  const int bi = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = bi * blk_k;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + blk_k);
+  const int cg = threadIdx.x % TPR;
+  const int64_t sh = (int64_t)s * H + h;
+  float mean[8];
+  if constexpr (FOLD) {
+    __shared__ float kmean[D];
+    const int c = threadIdx.x % D, g = threadIdx.x / D;
+    const double sum = sum_partials<D>(part + sh * nbq * D + c, (L + blk_q - 1) / blk_q, c, g);
+    if (g == 0) {
+      const float mv = (float)(sum / (double)L);
+      kmean[c] = mv;
+      if (bi == 0) km[sh * D + c] = mv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = kmean[cg * 8 + i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = km[sh * D + cg * 8 + i];
+  }
+  const float scale = quant_block<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, n1,
+                                     [&](float v, int i) { return v - mean[i]; },
+                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n);
+  if (threadIdx.x == 0) sk[sh * nbk + bi] = scale;
 }
 
 // ---------------------------------------------------------------- E4M3 V
@@ -248,27 +359,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
     }                                    \
   } while (0)
 
-hipError_t launch_k_colsum(const Problem& p, const void* K, Str ks, double* partial, hipStream_t st) {
-  dim3 grid(p.nchunk, p.heads, p.nseq);
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_colsum<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.nchunk, partial));
+// Heads with at most this many Q blocks fold the mean into k_quant_k.
+constexpr int kFoldMaxBlocks = 64;
+
+hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                                 int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st) {
+  dim3 grid(2 * p.nbq, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_q_colsum<D>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen,
+                                                 p.blk_q, p.nbq, sm_scale, q8, q8s, q_scale, partial));
   return hipGetLastError();
 }
 
-hipError_t launch_k_mean(const Problem& p, const double* partial, float* k_mean, hipStream_t st) {
-  hipLaunchKernelGGL(k_mean_finalize, dim3(p.heads, p.nseq), dim3(p.head_dim), 0, st, partial, p.cu, p.max_seqlen,
-                     p.nchunk, k_mean);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_qk(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
-                           const float* k_mean, int8_t* q8, Str q8s, int8_t* k8, Str k8s, float* q_scale,
-                           float* k_scale, hipStream_t st) {
-  dim3 grid(p.nbq + p.nbk, p.heads, p.nseq);
-  SAGE_DISPATCH_D(p.head_dim,
-                  hipLaunchKernelGGL((k_quant_qk<D>), grid, dim3(kThreads), 0, st, (const _Float16*)Q, qs,
-                                     (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.blk_k, p.nbq, p.nbk,
-                                     sm_scale, k_mean, q8, q8s, k8, k8s, q_scale, k_scale));
+hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
+                          Str k8s, float* k_scale, hipStream_t st) {
+  dim3 grid(p.nbk, p.heads, p.nseq);
+  if (p.nbq <= kFoldMaxBlocks) {
+    SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kThreads), 0, st,
+                                                   (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
+                                                   p.nbq, partial, k_mean, k8, k8s, k_scale));
+    return hipGetLastError();
+  }
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kThreads), 0, st,
+                                                 partial, p.cu, p.max_seqlen, p.blk_q, p.nbq, k_mean));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
+                                                 p.nbq, partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
 }
 

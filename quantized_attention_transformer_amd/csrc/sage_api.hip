@@ -117,7 +117,7 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   w.sq = take((size_t)p->nseq * H * q.nbq * 4);
   w.sk = take((size_t)p->nseq * H * q.nbk * 4);
   w.km = take((size_t)p->nseq * H * d * 4);
-  w.colsum = take((size_t)p->nseq * H * q.nchunk * d * 8);
+  w.colsum = take((size_t)p->nseq * H * q.nbq * d * 8);
   if (pv_mode == SAGE_PV_FP8) {
     w.v8 = take((size_t)(T * H * d));
     w.sv = take((size_t)p->nseq * H * d * 4);
@@ -132,7 +132,7 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
 
 size_t quantize_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
-  return align_up((size_t)p->nseq * p->heads * q.nchunk * p->head_dim * 8);
+  return align_up((size_t)p->nseq * p->heads * q.nbq * p->head_dim * 8);
 }
 
 int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
@@ -141,11 +141,11 @@ int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const vo
   const sage::Problem q = to_internal(p);
   if (sm_scale <= 0.0f || !std::isfinite(sm_scale)) sm_scale = (float)(1.0 / std::sqrt((double)p->head_dim));
   hipError_t e;
-  if ((e = sage::launch_k_colsum(q, K, S(ks), colsum, st)) != hipSuccess) return hip_fail(e, "k_colsum launch");
-  if ((e = sage::launch_k_mean(q, colsum, k_mean, st)) != hipSuccess) return hip_fail(e, "k_mean launch");
-  if ((e = sage::launch_quant_qk(q, Q, S(qs), K, S(ks), sm_scale, k_mean, q8, S(q8s), k8, S(k8s), q_scale,
-                                 k_scale, st)) != hipSuccess)
-    return hip_fail(e, "quant_qk launch");
+  if ((e = sage::launch_quant_q_colsum(q, Q, S(qs), K, S(ks), sm_scale, q8, S(q8s), q_scale, colsum, st)) !=
+      hipSuccess)
+    return hip_fail(e, "quant_q_colsum launch");
+  if ((e = sage::launch_quant_k(q, K, S(ks), colsum, k_mean, k8, S(k8s), k_scale, st)) != hipSuccess)
+    return hip_fail(e, "quant_k launch");
   return SAGE_OK;
 }
 

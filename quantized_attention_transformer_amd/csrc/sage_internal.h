@@ -13,7 +13,7 @@ struct Str {
   int64_t s, h, n;
 };
 
-// Tokens per partial of the column reductions (K sums, V absmax).
+// Tokens per partial of the V column absmax.
 constexpr int kColChunk = 512;
 
 __device__ __forceinline__ int seq_len(const int32_t* cu, int s, int max_seqlen) {
@@ -32,11 +32,12 @@ struct Problem {
 };
 
 // ---- pre-pass (prepass.hip) ----
-hipError_t launch_k_colsum(const Problem& p, const void* K, Str ks, double* partial, hipStream_t st);
-hipError_t launch_k_mean(const Problem& p, const double* partial, float* k_mean, hipStream_t st);
-hipError_t launch_quant_qk(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
-                           const float* k_mean, int8_t* q8, Str q8s, int8_t* k8, Str k8s, float* q_scale,
-                           float* k_scale, hipStream_t st);
+// INT8 Q blocks, plus fp64 column sums of K over each Q block's rows (partial: nseq*heads*nbq*head_dim).
+hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                                 int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st);
+// k_mean = fp32(sum of the partials / L) per (sequence, head, channel), and INT8 K blocks of K - k_mean.
+hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
+                          Str k8s, float* k_scale, hipStream_t st);
 // v_scale = max|V| / 448 per (sequence, head, channel): zero fill, atomic column max, divide in place.
 hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* v_scale, hipStream_t st);
 hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st);

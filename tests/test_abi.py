@@ -48,14 +48,15 @@ def _ws(p, mode=0):
 def test_workspace_bytes_layout():
     rc, n = _ws(_prob())
     assert rc == 0
-    # int8 Q and K (2 x 32 KiB), scales, mean, fp64 column-sum partials; 256-byte aligned regions
-    assert n == 2 * 32768 + 256 + 256 + 512 + 1024
+    # int8 Q and K (2 x 32 KiB), scales, mean, fp64 column-sum partials (one per Q block:
+    # 2 heads x 4 blocks x 64 channels x 8 bytes); 256-byte aligned regions
+    assert n == 2 * 32768 + 256 + 256 + 512 + 4096
     rc8, n8 = _ws(_prob(), 1)
     assert rc8 == 0 and n8 == n + 32768 + 512
     # quantize-only workspace: the column-sum partials
     m = ctypes.c_size_t(0)
     assert sage.lib().sage_quantize_workspace_bytes(ctypes.byref(_prob()), ctypes.byref(m)) == 0
-    assert m.value == 1024
+    assert m.value == 4096
 
 
 @pytest.mark.parametrize("kw,status", [
