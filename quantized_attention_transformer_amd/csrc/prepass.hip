@@ -17,9 +17,11 @@
 //     is exact and the result is independent of the reduction order.  mean =
 //     fp32(sum / L) with one IEEE fp64 division.
 //   * Q' = fp32(Q * sm_scale), K' = fp32(K - mean): one rounding each.
-//   * scale = fp32(absmax / 127) and code = rint(fp32(x / scale)) use IEEE
-//     fp32 division (HIP's default correctly rounded divide) and the
-//     hardware round-half-to-even; absmax is exact in any order.
+//   * scale = fp32(absmax / 127) (IEEE fp32 division) and code =
+//     rint(fp32(x / scale)) with round-half-to-even; the quotient is taken
+//     through the hardware reciprocal except within 2^-13 of a half-integer,
+//     where the IEEE division decides (see quant_block); absmax is exact in
+//     any order.
 //   * E4M3 codes come from the hardware convert (round to nearest even).
 #include "sage_internal.h"
 
@@ -87,14 +89,35 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
                                              const BlockRows<D>* pre = nullptr) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR, R = 128 / RPP;
   const int tid = threadIdx.x, r = tid / TPR;
+  // code = rint(RN(x' / scale)).  |x' / scale| <= 127 (1 + 2^-23), so with
+  // y = rcp(scale) (at most 1 ulp off) q0 = RN(x' * y) is within 2^-15 of
+  // x' / scale, and RN(x' / scale) within 2^-17: when q0 is more than 2^-13
+  // from every half-integer, all three round to the same integer.  Lanes
+  // closer than that (about 1 element in 4000) take the IEEE division.
   auto codes = [&](const H8& x, float a, float scale) {
     uint32_t w[2] = {0u, 0u};
     if (a > 0.0f) {
+      const float y = __builtin_amdgcn_rcpf(scale);
+      float xv[8], rv[8];
+      bool near = false;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float qv = rintf(transform((float)x.v[i], i) / scale);
-        qv = fminf(127.0f, fmaxf(-127.0f, qv));
-        w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (i & 3));
+        xv[i] = transform((float)x.v[i], i);
+        const float qv = xv[i] * y;
+        rv[i] = __builtin_rintf(qv);
+        near |= fabsf(qv - rv[i]) > 0.5f - 0x1p-13f;
+      }
+      if (__builtin_expect(__any(near), 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float rq = rv[i];
+          if (fabsf(xv[i] * y - rq) > 0.5f - 0x1p-13f) rv[i] = __builtin_rintf(xv[i] / scale);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = __builtin_amdgcn_fmed3f(rv[i], -127.0f, 127.0f);
+        w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)c) << (8 * (i & 3));
       }
     }
     return make_uint2(w[0], w[1]);
