@@ -59,8 +59,9 @@
 // (E4M3(448 p) then does not depend on the order keys are visited) and O is
 // not rescaled: it keeps the first tile's maximum m0 as reference and each
 // tile's P enters the P.V MFMA with the exact per-lane E8M0 scale
-// 2^(m - m0).  l sums the fp16-rounded P fed to the MFMA (v_dot2) on the
-// fp16 path, the unquantised P on the FP8 path.
+// 2^(m - m0).  l sums the fp32 P before rounding (fp32 adds), except on the
+// fp16 path at D = 64, where it sums the fp16-rounded P fed to the MFMA
+// (v_dot2).
 #include <type_traits>
 
 #include "sage_internal.h"
@@ -512,18 +513,28 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       return __builtin_amdgcn_exp2f(arg);
     };
     if constexpr (!FP8) {
+      // Row sums.  On gfx950 v_dot2_f32_f16 barely advances while the other
+      // wave of the SIMD streams MFMAs (measured: ~4% of its rate; plain VALU
+      // ops keep ~80%), so at D = 128, where the matrix phase is as long as
+      // this one, the sums are fp32 adds over the unrounded P (four chains).
+      // At D = 64 the matrix phase is short and this phase is the longer one:
+      // the 16 dot2 over the fp16 P (two chains) cost less than 32 adds.
+      float ls[4] = {lsum, 0.0f, 0.0f, 0.0f};
       const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
-      float ls[2] = {lsum, 0.0f};  // two independent accumulation chains
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const v2h hp = {(_Float16)prob(u >> 1, 8 * (u & 1) + e), (_Float16)prob(u >> 1, 8 * (u & 1) + e + 1)};
-          ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2(hp, ones, ls[(e >> 1) & 1], false);
+          const float p0 = prob(u >> 1, 8 * (u & 1) + e), p1 = prob(u >> 1, 8 * (u & 1) + e + 1);
+          const v2h hp = {(_Float16)p0, (_Float16)p1};
+          if constexpr (D == 128)
+            ls[e >> 1] += p0 + p1;
+          else
+            ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2(hp, ones, ls[(e >> 1) & 1], false);
           pf[u][e] = hp[0];
           pf[u][e + 1] = hp[1];
         }
-      lsum = ls[0] + ls[1];
+      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
       // P is complete here, in this (vector) phase: otherwise the compiler
       // sinks the exponentials into the next matrix phase, next to their use
 #pragma unroll
