@@ -10,6 +10,12 @@ value = attention TOPS of the step = (4 B H N^2 d + 4 B H N^2 d / 2) / t.
 roofline = the dominant kernel (the non-causal fused attention) against the
 MI355X dense INT8 MFMA peak; its duration is measured live with HIP events
 on the stream it runs on.  cpu_baseline = the CPU oracle on the same step.
+timing = median and min of the per-launch HIP event times (fused kernel,
+non-causal and causal), the sage_quantize pre-pass against the HBM peak
+(algorithmic bytes: fp16 Q and K read once, int8 written, scales, mean), and
+sage_attn end to end (its own workspace); sclk_mhz = amd-smi's shader clock
+sampled while the kernel runs back to back.  inputs_sha256 = provenance of
+the synthetic fp16 Q, K, V.
 extra = kernel-only TOPS of the fused kernel on the larger workloads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -28,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
 FP16_PEAK_TFLOPS = 2500.0
+HBM_PEAK_BPS = 8.0e12            # MI355X HBM3E, published
 METRIC = "attention TOPS (4·B·H·N²·d/t) at d=128, N=4K–32K; % of INT8 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_text_noncausal_traffic.json")
 
@@ -111,16 +118,25 @@ def main():
                                    v.data_ptr(), s_in, None, out.data_ptr(), so, int(causal), 0, sp)
         assert rc == 0, L.sage_last_error()
 
-    ev = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for c in (False, True)}
+    def evpair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def step(i=None):
+    ev = {c: [evpair() for _ in range(args.steps)] for c in (False, True)}
+    evq = {c: [evpair() for _ in range(args.steps)] for c in (False, True)}
+
+    def step(i=None, quant_events=False):
+        # timed steps carry events around the fused kernel only; the pre-pass
+        # is timed in a separate pass of the same steps
         for causal in (False, True):
+            if quant_events:
+                evq[causal][i][0].record(stream)
             quantize()
-            if i is not None:
+            if quant_events:
+                evq[causal][i][1].record(stream)
+            elif i is not None:
                 ev[causal][i][0].record(stream)
             attention(causal)
-            if i is not None:
+            if i is not None and not quant_events:
                 ev[causal][i][1].record(stream)
 
     if args.copy_calib:
@@ -139,13 +155,22 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    for i in range(args.steps):
+        step(i, quant_events=True)
+    torch.cuda.synchronize()
     ms_step = total_ms / args.steps
     ops_nc = sage.attention_ops([N] * B, H, d, False)
     ops_c = sage.attention_ops([N] * B, H, d, True)
     value = (ops_nc + ops_c) / (ms_step * 1e-3) / 1e12
-    kern_nc = float(np.mean([a.elapsed_time(b) for a, b in ev[False]]))
-    kern_c = float(np.mean([a.elapsed_time(b) for a, b in ev[True]]))
+    t_attn = {c: np.array([a.elapsed_time(b) for a, b in ev[c]]) for c in (False, True)}
+    t_quant = np.concatenate([[a.elapsed_time(b) for a, b in evq[c]] for c in (False, True)])
+    kern_nc = float(t_attn[False].mean())
+    kern_c = float(t_attn[True].mean())
     achieved = ops_nc / (kern_nc * 1e-3) / 1e12
+    nbq, nbk = -(-N // wl.blk_q), -(-N // wl.blk_k)
+    # algorithmic bytes of sage_quantize: fp16 Q and K read once, int8 written, plus scales and the mean
+    quant_bytes = 3 * 2 * B * N * H * d + 4 * B * H * (nbq + nbk) + 4 * B * H * d
+    q_med = float(np.median(t_quant))
 
     result = {
         "metric": METRIC,
@@ -171,13 +196,80 @@ def main():
                      "mixed_ceiling_frac": round(2 / 3, 4)},
     }
 
+    result["timing"] = {
+        "attn_kernel_ms": {("causal" if c else "noncausal"): {"median": round(float(np.median(t_attn[c])), 5),
+                                                              "min": round(float(t_attn[c].min()), 5)}
+                           for c in (False, True)},
+        "prepass": {"call": "sage_quantize (2 launches: Q quantisation + K column sums, then K quantisation)",
+                    "ms_median": round(q_med, 5), "ms_min": round(float(t_quant.min()), 5),
+                    "algorithmic_bytes": quant_bytes, "GB/s": round(quant_bytes / (q_med * 1e-3) / 1e9, 1),
+                    "frac_hbm_peak": round(quant_bytes / (q_med * 1e-3) / HBM_PEAK_BPS, 4)},
+        "sage_attn_end_to_end": end_to_end(sage, torch, q, k, v, wl, ops_nc, ops_c),
+    }
+    result["inputs_sha256"] = {n: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+                               for n, a in (("q", inp.q), ("k", inp.k), ("v", inp.v))}
+
     if not args.no_extra:
         result["extra"] = extra_workloads(sage, torch, dev)
+        result["timing"]["sclk_mhz"] = sample_sclk(lambda: attention(False), torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, ops_nc + ops_c)
 
     print(json.dumps(result), flush=True)
+
+
+def end_to_end(sage, torch, q, k, v, wl, ops_nc, ops_c, warmup=10, runs=50):
+    """sage_attn (quantisation + attention in one call, its own workspace) on
+    the step's inputs: median and min over single-call HIP event timings."""
+    import numpy as np
+    out = torch.empty_like(q)
+    ws = torch.empty(max(16, sage.workspace_bytes(sage.make_problem(q, "bnhd", blk_q=wl.blk_q, blk_k=wl.blk_k))),
+                     dtype=torch.uint8, device=q.device)
+    res = {}
+    for causal, ops in ((False, ops_nc), (True, ops_c)):
+        def run():
+            sage.attn(q, k, v, causal=causal, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out, workspace=ws)
+        for _ in range(warmup):
+            run()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        for a, b in evs:
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        med = float(np.median(t))
+        res["causal" if causal else "noncausal"] = {"ms_median": round(med, 5), "ms_min": round(float(t.min()), 5),
+                                                    "TOPS": round(ops / (med * 1e-3) / 1e12, 1)}
+    return res
+
+
+def sample_sclk(run, torch, max_s=8.0):
+    """Shader clock while the fused kernel runs back to back: `amd-smi metric -c`
+    sampled once under load (mean and range over the XCDs), or the error."""
+    import subprocess
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError as e:
+        return {"error": str(e)}
+    t0 = time.time()
+    while proc.poll() is None and time.time() - t0 < max_s:
+        for _ in range(200):
+            run()
+        torch.cuda.synchronize()
+    try:
+        txt, _ = proc.communicate(timeout=10)
+        data = json.loads(txt)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clks = [v["clk"]["value"] for kk, v in gpu["clock"].items() if kk.startswith("gfx") and isinstance(v, dict)]
+        clks = [float(c) for c in clks if isinstance(c, (int, float))]
+        return {"mean": round(sum(clks) / len(clks), 1), "min": min(clks), "max": max(clks), "xcds": len(clks),
+                "source": "amd-smi metric -c, sampled once while the non-causal kernel ran back to back"}
+    except Exception as e:  # noqa: BLE001  (report, never fail the bench over the clock reading)
+        proc.kill()
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def extra_workloads(sage, torch, dev):

@@ -28,7 +28,7 @@
 namespace sage {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // E4M3 V kernels
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -36,15 +36,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Block-wide max of a non-negative value (kThreads threads).
+// Block-wide max of a non-negative value (NTH threads).
+template <int NTH>
 __device__ __forceinline__ float block_max(float v) {
-  __shared__ float wm[kThreads / 64];
+  __shared__ float wm[NTH / 64];
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = v;
   __syncthreads();
   float r = wm[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, wm[i]);
+  for (int i = 1; i < NTH / 64; ++i) r = fmaxf(r, wm[i]);
   return r;
 }
 
@@ -59,12 +60,21 @@ __device__ __forceinline__ H8 load_h8(const _Float16* p) {
 }
 
 // ---------------------------------------------------------------- INT8 blocks
+// The INT8 kernels run 512 threads (8 waves, two per SIMD): a text-sized head
+// gives one block per CU, and the per-element work then spreads over twice
+// the waves.
+constexpr int kQThreads = 512;
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: M + r for an integer |r| < 2^22 is exact,
+                                       // and its bit pattern's low byte is r as int8
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
 // Rows of a block of up to 128 rows held in registers: thread (r, cg) holds
 // rows n0 + r + RPP*j, j < R, channels 8cg .. 8cg+7.  All loads are issued
 // before any is used, so the block costs one memory round trip.
 template <int D>
 struct BlockRows {
-  static constexpr int TPR = D / 8, RPP = kThreads / TPR, R = 128 / RPP;
+  static constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
   H8 x[R];
   __device__ __forceinline__ void load(const _Float16* __restrict__ src, int64_t sn, int n0, int n1) {
     const int r = threadIdx.x / TPR;
@@ -76,97 +86,131 @@ struct BlockRows {
   }
 };
 
+// Per-channel maximum and minimum of rows, in fp16 (packed pairs: exact).
+struct Extremes {
+  v2h hi[4], lo[4];
+  __device__ __forceinline__ Extremes() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = v2h{(_Float16)-INFINITY, (_Float16)-INFINITY};
+      lo[i] = v2h{(_Float16)INFINITY, (_Float16)INFINITY};
+    }
+  }
+  __device__ __forceinline__ void add(const H8& x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v2h p = {x.v[2 * i], x.v[2 * i + 1]};
+      hi[i] = __builtin_elementwise_max(hi[i], p);
+      lo[i] = __builtin_elementwise_min(lo[i], p);
+    }
+  }
+  // max over the 8 channels of |T(x)| for T monotone non-decreasing: the
+  // extremes of T(x) over the rows are T(max) and T(min)
+  template <typename F>
+  __device__ __forceinline__ float absmax(F transform) const {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float h = transform((float)hi[i >> 1][i & 1], i), l = transform((float)lo[i >> 1][i & 1], i);
+      a = fmaxf(a, fmaxf(fabsf(h), fabsf(l)));
+    }
+    return a;
+  }
+};
+
+// INT8 codes of one row chunk (8 channels): x' = transform(x) (one fp32
+// rounding), code = rint(fp32(x' / scale)) with round-half-to-even.  With y =
+// rcp(scale) (at most 1 ulp off) the exact product x' * y is within 2^-16 of
+// x' / scale, and fp32(x' / scale) within 2^-17 of it (|x' / scale| < 127.5):
+// when x' * y is more than 2^-15 from every half-integer, all of them round
+// to the same integer.  fma(x', y, M) with M = 1.5 * 2^23 rounds x' * y to
+// that integer r (ties to even; M is even), and fma(x', y, -r) gives the
+// residual to within 2^-25; lanes with |residual| > 1/2 - 2^-13 (about 1
+// element in 4000) take the IEEE division instead.  |r| <= 127 always (x' <=
+// absmax and the errors above stay far below 1/2), so the code is the low
+// byte of M + r.
+template <typename F>
+__device__ __forceinline__ uint2 codes8(const H8& x, F transform, float scale, float y) {
+  float xv[8], tv[8];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xv[i] = transform((float)x.v[i], i);
+    tv[i] = __builtin_fmaf(xv[i], y, kMagic);
+    near |= fabsf(__builtin_fmaf(xv[i], y, kMagic - tv[i])) > 0.5f - 0x1p-13f;
+  }
+  if (__builtin_expect(__any(near), 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (fabsf(__builtin_fmaf(xv[i], y, kMagic - tv[i])) > 0.5f - 0x1p-13f)
+        tv[i] = __builtin_rintf(xv[i] / scale) + kMagic;
+  }
+  uint32_t t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = __float_as_uint(tv[i]);
+  // low bytes: [t0 t1 t2 t3], [t4 t5 t6 t7]
+  const uint32_t w0 = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
+  const uint32_t w1 = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[6], 0x04000c0cu);
+  return make_uint2(w0, w1);
+}
+
 // One quantisation block, rows [n0, n1) of one (sequence, head): thread (r,
 // cg) handles rows n0 + r + RPP*j, channels 8cg .. 8cg+7 (16-byte loads).
-// x' = transform(x) (one fp32 rounding), scale = fp32(absmax / 127), code =
-// rint(x' / scale) clipped to +-127 (0 when the block is all zero).  Blocks
-// of up to 128 rows stay in registers between the absmax and the codes (one
-// read of HBM; `pre`: already loaded); longer ones are read twice.  Returns
-// the scale.
+// transform must be monotone non-decreasing (x * sm_scale with sm_scale > 0,
+// or x - mean): the block's absmax of x' then comes from the per-channel fp16
+// maximum and minimum.  scale = fp32(absmax / 127); codes as in codes8 (0 when
+// the block is all zero).  Blocks of up to 128 rows stay in registers between
+// the absmax and the codes (one read of HBM; `pre`: already loaded); longer
+// ones are read twice.  Returns the scale.
 template <int D, typename F>
 __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, int64_t sn, int n0, int n1,
                                              F transform, int8_t* __restrict__ dst, int64_t dn,
                                              const BlockRows<D>* pre = nullptr) {
-  constexpr int TPR = D / 8, RPP = kThreads / TPR, R = 128 / RPP;
-  const int tid = threadIdx.x, r = tid / TPR;
-  // code = rint(RN(x' / scale)).  |x' / scale| <= 127 (1 + 2^-23), so with
-  // y = rcp(scale) (at most 1 ulp off) q0 = RN(x' * y) is within 2^-15 of
-  // x' / scale, and RN(x' / scale) within 2^-17: when q0 is more than 2^-13
-  // from every half-integer, all three round to the same integer.  Lanes
-  // closer than that (about 1 element in 4000) take the IEEE division.
-  auto codes = [&](const H8& x, float a, float scale) {
-    uint32_t w[2] = {0u, 0u};
-    if (a > 0.0f) {
-      const float y = __builtin_amdgcn_rcpf(scale);
-      float xv[8], rv[8];
-      bool near = false;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xv[i] = transform((float)x.v[i], i);
-        const float qv = xv[i] * y;
-        rv[i] = __builtin_rintf(qv);
-        near |= fabsf(qv - rv[i]) > 0.5f - 0x1p-13f;
-      }
-      if (__builtin_expect(__any(near), 0)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float rq = rv[i];
-          if (fabsf(xv[i] * y - rq) > 0.5f - 0x1p-13f) rv[i] = __builtin_rintf(xv[i] / scale);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float c = __builtin_amdgcn_fmed3f(rv[i], -127.0f, 127.0f);
-        w[i >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)c) << (8 * (i & 3));
-      }
-    }
-    return make_uint2(w[0], w[1]);
-  };
-  float amax = 0.0f;
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
+  const int r = threadIdx.x / TPR;
+  Extremes ex;
   if (n1 - n0 <= RPP * R) {
     BlockRows<D> rows;
     if (pre)
       rows = *pre;
     else
       rows.load(src, sn, n0, n1);
-    const H8* x = rows.x;
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      if (n0 + r + RPP * j < n1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x[j].v[i], i)));
-    const float a = block_max(amax);
+      if (n0 + r + RPP * j < n1) ex.add(rows.x[j]);
+    const float a = block_max<kQThreads>(n0 + r < n1 ? ex.absmax(transform) : 0.0f);
     const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+    const float y = __builtin_amdgcn_rcpf(scale);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int n = n0 + r + RPP * j;
-      if (n < n1) *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) = codes(x[j], a, scale);
+      if (n < n1)
+        *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) =
+            a > 0.0f ? codes8(rows.x[j], transform, scale, y) : make_uint2(0u, 0u);
     }
     return scale;
   }
 #pragma unroll 2
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(src + (int64_t)n * sn);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(transform((float)x.v[i], i)));
-  }
-  const float a = block_max(amax);
+  for (int n = n0 + r; n < n1; n += RPP) ex.add(load_h8(src + (int64_t)n * sn));
+  const float a = block_max<kQThreads>(n0 + r < n1 ? ex.absmax(transform) : 0.0f);
   const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+  const float y = __builtin_amdgcn_rcpf(scale);
 #pragma unroll 2
   for (int n = n0 + r; n < n1; n += RPP)
-    *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) = codes(load_h8(src + (int64_t)n * sn), a, scale);
+    *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) =
+        a > 0.0f ? codes8(load_h8(src + (int64_t)n * sn), transform, scale, y) : make_uint2(0u, 0u);
   return scale;
 }
 
-// grid (2*nbq, heads, nseq): workgroup 2bi quantises Q block bi (INT8 Q' = Q *
-// sm_scale); workgroup 2bi+1 takes the fp64 column sums of K over the same
-// rows, one partial per Q block.
+// grid (2*nbq, heads, nseq), kQThreads: workgroup 2bi quantises Q block bi
+// (INT8 Q' = Q * sm_scale); workgroup 2bi+1 takes the fp64 column sums of K
+// over the same rows, one partial per Q block.
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_quant_q_colsum(
+__global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
     int max_seqlen, int blk_q, int nbq, float sm_scale, int8_t* __restrict__ q8, Str q8s, float* __restrict__ sq,
     double* __restrict__ part) {
-  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int bi = blockIdx.x >> 1, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int L = seq_len(cu, s, max_seqlen);
   const int n0 = bi * blk_q;
@@ -213,10 +257,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_q_colsum(
 }
 
 // Sum of the nb = ceil(L / blk_q) partials of channel c of (s, h), by the
-// kThreads / D threads of c (16 independent loads per round), combined in LDS.
+// kQThreads / D threads of c (16 independent loads per round), combined in LDS.
 template <int D>
 __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, int nb, int c, int g) {
-  constexpr int G = kThreads / D;
+  constexpr int G = kQThreads / D;
   double tot = 0.0;
   for (int k0 = g; k0 < nb; k0 += 16 * G) {
     double t[16];
@@ -237,12 +281,12 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
   return sum;
 }
 
-// grid (heads, nseq), kThreads: mean = fp32(sum / L) from the per-Q-block
+// grid (heads, nseq), kQThreads: mean = fp32(sum / L) from the per-Q-block
 // partials (long sequences; shorter ones fold this into k_quant_k).
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_mean_finalize(const double* __restrict__ part,
-                                                            const int32_t* __restrict__ cu, int max_seqlen, int blk_q,
-                                                            int nbq, float* __restrict__ km) {
+__global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
+                                                             const int32_t* __restrict__ cu, int max_seqlen,
+                                                             int blk_q, int nbq, float* __restrict__ km) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
   const int L = seq_len(cu, s, max_seqlen);
   const int nb = (L + blk_q - 1) / blk_q;
@@ -250,15 +294,16 @@ __global__ __launch_bounds__(kThreads) void k_mean_finalize(const double* __rest
   if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(sum / (double)L) : 0.0f;
 }
 
-// grid (nbk, heads, nseq): K block bi -> INT8 K' = K - mean(K).  FOLD: the
-// workgroup sums the column partials itself (every block of the head does;
-// block 0 stores k_mean), otherwise k_mean comes from k_mean_finalize.
+// grid (nbk, heads, nseq), kQThreads: K block bi -> INT8 K' = K - mean(K).
+// FOLD: the workgroup sums the column partials itself (every block of the
+// head does; block 0 stores k_mean), with the block's K rows already in
+// flight; otherwise k_mean comes from k_mean_finalize.
 template <int D, bool FOLD>
-__global__ __launch_bounds__(kThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
-                                                      const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
-                                                      int nbk, int blk_q, int nbq, const double* __restrict__ part,
-                                                      float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
-                                                      float* __restrict__ sk) {
+__global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
+                                                       int nbk, int blk_q, int nbq, const double* __restrict__ part,
+                                                       float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
+                                                       float* __restrict__ sk) {
   constexpr int TPR = D / 8;
   const int bi = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int L = seq_len(cu, s, max_seqlen);
@@ -267,6 +312,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_k(const _Float16* __restrict
   const int n1 = min(L, n0 + blk_k);
   const int cg = threadIdx.x % TPR;
   const int64_t sh = (int64_t)s * H + h;
+  const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
+  BlockRows<D> krows;
+  const bool pre = n1 - n0 <= 128;
+  if (pre) krows.load(kb, ks.n, n0, n1);
   float mean[8];
   if constexpr (FOLD) {
     __shared__ float kmean[D];
@@ -284,9 +333,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_k(const _Float16* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) mean[i] = km[sh * D + cg * 8 + i];
   }
-  const float scale = quant_block<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, n1,
-                                     [&](float v, int i) { return v - mean[i]; },
-                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n);
+  const float scale = quant_block<D>(kb, ks.n, n0, n1, [&](float v, int i) { return v - mean[i]; },
+                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n, pre ? &krows : nullptr);
   if (threadIdx.x == 0) sk[sh * nbk + bi] = scale;
 }
 
@@ -388,7 +436,7 @@ constexpr int kFoldMaxBlocks = 64;
 hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st) {
   dim3 grid(2 * p.nbq, p.heads, p.nseq);
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_q_colsum<D>), grid, dim3(kThreads), 0, st,
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_q_colsum<D>), grid, dim3(kQThreads), 0, st,
                                                  (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen,
                                                  p.blk_q, p.nbq, sm_scale, q8, q8s, q_scale, partial));
   return hipGetLastError();
@@ -398,16 +446,16 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
                           Str k8s, float* k_scale, hipStream_t st) {
   dim3 grid(p.nbk, p.heads, p.nseq);
   if (p.nbq <= kFoldMaxBlocks) {
-    SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kThreads), 0, st,
+    SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
                                                    (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
                                                    p.nbq, partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kThreads), 0, st,
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st,
                                                  partial, p.cu, p.max_seqlen, p.blk_q, p.nbq, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kThreads), 0, st,
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
                                                  (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
                                                  p.nbq, partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
