@@ -143,6 +143,17 @@ int sage_debug_qk_i32(const sage_problem* p,
                       const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
                       int32_t* s_out, void* stream);
 
+/* Debug: one issue of the FP8 P.V instruction (v_mfma_scale_f32_32x32x64_f8f6f4)
+ * on given operands, to check its arithmetic, e.g. the accumulator precision
+ * ([SA2] 技术方案 item 3 reports an accumulator narrower than FP32 for the
+ * FP8 matrix instruction of other hardware):
+ *   D = (A . B) * 2^(scale_a - 127) * 2^(scale_b - 127) + C
+ * A [32][64] and B [64][32] are OCP E4M3 codes, C and D fp32 [32][32], all
+ * row-major device arrays (D may not alias the inputs); scale_a, scale_b are
+ * E8M0 exponents in [0, 254].  One wave; asynchronous on `stream`. */
+int sage_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int scale_a, int scale_b, float* d,
+                        void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* sage_last_error(void);
 

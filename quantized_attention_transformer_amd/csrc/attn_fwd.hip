@@ -912,10 +912,46 @@ hipError_t launch_d(const Problem& p, const AttnArgs& a, bool causal, bool fp8, 
   return causal ? launch_ks<D, false, true>(p, a, st) : launch_ks<D, false, false>(p, a, st);
 }
 
+// One wave: D = A . B * 2^(sa - 127) * 2^(sb - 127) + C with the FP8 P.V
+// instruction, operands in the fused kernel's layout: lane (m, g = lane/32)
+// holds A[m][32g .. 32g+31] and B[32g .. 32g+31][m]; accumulator r of lane
+// (n, g) is D[8(r/4) + 4g + r%4][n].  A [32][64] and B [64][32] E4M3 codes, C
+// and D fp32 [32][32], all row-major.
+__global__ __launch_bounds__(64) void k_debug_fp8_mfma(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                       const float* __restrict__ C, int sa, int sb,
+                                                       float* __restrict__ Dout) {
+  const int lane = threadIdx.x, m = lane & 31, g = lane >> 5;
+  v8i av, bv;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t wa = 0, wb = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = 32 * g + 4 * j + t;
+      wa |= (uint32_t)A[m * 64 + k] << (8 * t);
+      wb |= (uint32_t)B[k * 32 + m] << (8 * t);
+    }
+    av[j] = (int)wa;
+    bv[j] = (int)wb;
+  }
+  v16f acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = C[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + m];
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, sa, 0, sb);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Dout[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + m] = acc[r];
+}
+
 }  // namespace
 
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
   return p.head_dim == 64 ? launch_d<64>(p, a, causal, fp8, st) : launch_d<128>(p, a, causal, fp8, st);
+}
+
+hipError_t launch_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int sa, int sb, float* d,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(k_debug_fp8_mfma, dim3(1), dim3(64), 0, st, a, b, c, sa, sb, d);
+  return hipGetLastError();
 }
 
 }  // namespace sage

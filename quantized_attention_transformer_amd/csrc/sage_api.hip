@@ -287,4 +287,14 @@ int sage_debug_qk_i32(const sage_problem* p, const int8_t* q8, sage_strides q8s,
   return SAGE_OK;
 }
 
+int sage_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int scale_a, int scale_b, float* d,
+                        void* stream) {
+  if (!a || !b || !c || !d) return fail(SAGE_ERR_INVALID_ARG, "operands must not be NULL");
+  if (scale_a < 0 || scale_a > 254 || scale_b < 0 || scale_b > 254)
+    return fail(SAGE_ERR_INVALID_ARG, "E8M0 scales must be in [0, 254] (%d, %d)", scale_a, scale_b);
+  hipError_t e = sage::launch_debug_fp8_mfma(a, b, c, scale_a, scale_b, d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug fp8 mfma launch");
+  return SAGE_OK;
+}
+
 }  // extern "C"

@@ -60,5 +60,8 @@ struct AttnArgs {
   int32_t* dump;  // debug i32 scores or nullptr
 };
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
+// One FP8 P.V MFMA on given operands (debug; one wave).
+hipError_t launch_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int sa, int sb, float* d,
+                                 hipStream_t st);
 
 }  // namespace sage

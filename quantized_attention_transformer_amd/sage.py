@@ -25,7 +25,7 @@ SAGE_PV_FP16 = 0
 SAGE_PV_FP8 = 1
 
 EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quantize", "sage_quantize_v_fp8",
-            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_last_error")
+            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma", "sage_last_error")
 
 
 class Strides(ctypes.Structure):
@@ -60,6 +60,7 @@ def lib():
         L.sage_attn_quantized.argtypes = [P, vp, S, vp, S, vp, vp, vp, S, vp, vp, S, i32, i32, vp]
         L.sage_attn.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp, sz, vp]
         L.sage_debug_qk_i32.argtypes = [P, vp, S, vp, S, vp, vp]
+        L.sage_debug_fp8_mfma.argtypes = [vp, vp, vp, i32, i32, vp, vp]
         L.sage_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
             if name != "sage_last_error":
@@ -209,3 +210,18 @@ def attention_ops(seqlens, heads: int, head_dim: int, causal: bool) -> float:
 
 def default_sm_scale(d: int) -> float:
     return float(1.0 / math.sqrt(d))
+
+
+def debug_fp8_mfma(a8: torch.Tensor, b8: torch.Tensor, c: torch.Tensor, scale_a: int = 127, scale_b: int = 127):
+    """sage_debug_fp8_mfma: D = A . B * 2^(scale_a-127) * 2^(scale_b-127) + C on the
+    FP8 P.V instruction.  a8 uint8 [32, 64], b8 uint8 [64, 32] (E4M3 codes), c fp32
+    [32, 32], all contiguous on the device; returns D fp32 [32, 32]."""
+    if a8.shape != (32, 64) or b8.shape != (64, 32) or c.shape != (32, 32):
+        raise ValueError("shapes must be A [32, 64], B [64, 32], C [32, 32]")
+    if a8.dtype != torch.uint8 or b8.dtype != torch.uint8 or c.dtype != torch.float32:
+        raise ValueError("A and B are uint8 E4M3 codes, C is float32")
+    a8, b8, c = a8.contiguous(), b8.contiguous(), c.contiguous()
+    d = torch.empty((32, 32), dtype=torch.float32, device=c.device)
+    _check("sage_debug_fp8_mfma", lib().sage_debug_fp8_mfma(_ptr(a8), _ptr(b8), _ptr(c), int(scale_a), int(scale_b),
+                                                           _ptr(d), _stream()))
+    return d
