@@ -228,33 +228,41 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
-def quant_v_fp8_seq(v_seq: np.ndarray):
-    """V of one (sequence, head) -> (e4m3 codes [L, d], fp32 scale [d]);
-    scale = fp32(max_n |V| / 448) per channel ([SA2] 技术方案 item 4), codes =
-    E4M3(fp32(V / scale)); a channel that is all zero gets scale 0, codes 0."""
+def quant_v_fp8_seq(v_seq: np.ndarray, smooth: bool = False):
+    """V of one (sequence, head) -> (e4m3 codes [L, d], fp32 scale [d], fp32
+    mean [d]).  Without smoothing: scale = fp32(max_n |V| / 448) per channel
+    ([SA2] 技术方案 item 4), codes = E4M3(fp32(V / scale)), mean 0.  With
+    smoothing (the optional smooth-V step described after 技术方案 on the same
+    page): mean = mean(V) over the tokens per channel (exact, as for K), V' =
+    fp32(V - mean), then the same scale and codes on V'.  A channel that is
+    all zero (after smoothing: constant) gets scale 0 and codes 0."""
     vf = v_seq.astype(np.float32)
+    vm = k_mean(v_seq) if smooth else np.zeros(vf.shape[1], np.float32)
+    if smooth:
+        vf = (vf - vm[None, :]).astype(np.float32)
     a = np.max(np.abs(vf), axis=0) if vf.shape[0] else np.zeros(vf.shape[1], np.float32)
     sv = (a / np.float32(448)).astype(np.float32)
     safe = np.where(sv == 0, np.float32(1), sv)
     r = (vf / safe[None, :]).astype(np.float32)
     codes = e4m3_encode(r)
     codes[:, sv == 0] = 0
-    return codes, sv
+    return codes, sv, vm
 
 
-def quant_v_fp8(v: np.ndarray, seqlens, cu):
-    """quant_v_fp8_seq for every (sequence, head); returns codes in V's layout
-    and scales [nseq, H, d]."""
+def quant_v_fp8(v: np.ndarray, seqlens, cu, smooth: bool = False):
+    """quant_v_fp8_seq for every (sequence, head); returns codes in V's layout,
+    scales [nseq, H, d] and means [nseq, H, d] (zero without smoothing)."""
     nseq = len(seqlens)
     H, d = v.shape[-2], v.shape[-1]
     v8 = np.zeros(v.shape, np.uint8)
     sv = np.zeros((nseq, H, d), np.float32)
+    vm = np.zeros((nseq, H, d), np.float32)
     vv, v8v = _seq_views(v, cu, nseq), _seq_views(v8, cu, nseq)
     for s in range(nseq):
         L = int(seqlens[s])
         for h in range(H):
-            v8v[s][:L, h, :], sv[s, h] = quant_v_fp8_seq(vv[s][:L, h, :])
-    return v8, sv
+            v8v[s][:L, h, :], sv[s, h], vm[s, h] = quant_v_fp8_seq(vv[s][:L, h, :], smooth)
+    return v8, sv, vm
 
 
 # --------------------------------------------------------------------------
@@ -277,9 +285,11 @@ def fp8_probs(S):
 
 
 def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
-                   pv_fp8=False, v8h=None, svh=None, return_lse=False):
+                   pv_fp8=False, v8h=None, svh=None, return_lse=False, vmh=None):
     """One (sequence, head).  q8h, k8h: int8 [L, d]; sqh, skh: per-block scales;
-    vh: fp16 [L, d]; rows: query indices to compute (default all).
+    vh: fp16 [L, d]; rows: query indices to compute (default all); FP8 path:
+    v8h, svh and, with smooth V, vmh (the mean added back to O: every row of
+    P sums to 1, so P V = P (V - mean) + mean).
     Returns O fp64 [len(rows), d]."""
     L = q8h.shape[0]
     rows = np.arange(L) if rows is None else np.asarray(rows)
@@ -301,23 +311,27 @@ def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
         p8 = e4m3_decode(e4m3_encode(P * 448.0))
         vd = e4m3_decode(v8h)
         O = (p8 @ vd) * (svh.astype(np.float64)[None, :] / 448.0) / l
+        if vmh is not None:
+            O = O + vmh.astype(np.float64)[None, :]
     if return_lse:
         return O, (m[:, 0] + np.log(l[:, 0]))
     return O
 
 
 def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=False,
-              rows_by_seq=None, smooth=True, quant=None):
+              rows_by_seq=None, smooth=True, quant=None, smooth_v=False):
     """The whole forward pass.  Layouts as in quantize_qk.  rows_by_seq
     optionally maps a sequence index to the query rows to compute (the rest
-    of O is left NaN).  Returns (O fp64 in Q's layout, quantisation dict)."""
+    of O is left NaN).  smooth_v (FP8 path): subtract mean(V) before the E4M3
+    quantisation and add it to O.  Returns (O fp64 in Q's layout,
+    quantisation dict)."""
     nseq = len(seqlens)
     H = q.shape[-2]
     qd = quant if quant is not None else quantize_qk(q, k, seqlens, cu, blk_q, blk_k, sm_scale,
                                                      smooth=smooth)
     if pv_fp8:
-        v8, sv = quant_v_fp8(v, seqlens, cu)
-        qd = dict(qd, v8=v8, sv=sv)
+        v8, sv, vm = quant_v_fp8(v, seqlens, cu, smooth_v)
+        qd = dict(qd, v8=v8, sv=sv, vm=vm)
     O = np.full(q.shape, np.nan, np.float64)
     ov = _seq_views(O, cu, nseq)
     q8v, k8v, vv = (_seq_views(a, cu, nseq) for a in (qd["q8"], qd["k8"], v))
@@ -331,7 +345,8 @@ def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=
             o = attention_head(q8v[s][:L, h], k8v[s][:L, h], qd["sq"][s, h], qd["sk"][s, h],
                                vv[s][:L, h], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8,
                                v8h=None if v8v is None else v8v[s][:L, h],
-                               svh=None if v8v is None else qd["sv"][s, h])
+                               svh=None if v8v is None else qd["sv"][s, h],
+                               vmh=qd["vm"][s, h] if (pv_fp8 and smooth_v) else None)
             if rows is None:
                 ov[s][:L, h] = o
             else:

@@ -88,7 +88,7 @@ def test_e4m3_convert_matches_oracle_on_every_code_and_tie():
     v[0, 1:, 0, :] = flat.reshape(L - 1, d)
     v8, sv = S().quantize_v_fp8(dev(v))
     assert (host(sv) == 1.0).all()
-    want, _ = O.quant_v_fp8(v, [L], None)
+    want, _, _ = O.quant_v_fp8(v, [L], None)
     np.testing.assert_array_equal(host(v8), want)
 
 
@@ -120,7 +120,7 @@ def test_quantize_bitexact_full_size(wl):
 def test_quantize_v_fp8_bitexact(wl, kw):
     inp = synth.generate(wl, **kw)
     v8, sv = S().quantize_v_fp8(dev(inp.v), **gpu_kwargs(inp))
-    rv8, rsv = O.quant_v_fp8(inp.v, inp.seqlens, inp.cu_seqlens)
+    rv8, rsv, _ = O.quant_v_fp8(inp.v, inp.seqlens, inp.cu_seqlens)
     np.testing.assert_array_equal(host(sv), rsv)
     g8 = host(v8)
     if inp.cu_seqlens is None:

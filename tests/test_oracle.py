@@ -357,3 +357,73 @@ def test_fp8_oracle_close_to_fp16_oracle():
     # the V scale is per (sequence, head, channel) and maps the absmax to 448
     vd = O.e4m3_decode(qd["v8"][0, :, 0, :])
     assert np.abs(vd).max() == 448.0
+
+
+# ---------------------------------------------------------------- smooth V (FP8 P.V path)
+
+def test_ex_f_smooth_v():
+    g = GOLD["ex_f_smooth_v"]
+    v = np.array(g["v"], np.float16)
+    codes, sv, vm = O.quant_v_fp8_seq(v, smooth=True)
+    np.testing.assert_array_equal(vm, np.array(g["mean"], np.float32))
+    assert [hex(int(b)) for b in sv.view(np.uint32)] == [hex(int(x, 16)) for x in g["scale_bits"]]
+    np.testing.assert_array_equal(codes, np.array(g["codes"], np.uint8))
+    # exact re-derivation: mean, V' = RN32(V - mean), scale = RN32(max|V'| / 448),
+    # code = E4M3(RN32(V' / scale))
+    for c in range(v.shape[1]):
+        col = [Fraction(float(x)) for x in v[:, c]]
+        mean = rn32(sum(col) / len(col))
+        assert mean == Fraction(float(vm[c]))
+        vs = [rn32(x - mean) for x in col]
+        a = max(abs(x) for x in vs)
+        sc = rn32(a / 448)
+        assert sc == Fraction(float(sv[c]))
+        want = [0 if sc == 0 else e4m3_round(rn32(x / sc)) for x in vs]
+        assert want == [int(x) for x in codes[:, c]]
+
+
+def test_smooth_v_is_exact_in_fp64():
+    # every row of the softmax sums to 1, so softmax(S) V = softmax(S) (V - m) + m
+    rng = np.random.default_rng(21)
+    L, H, d = 96, 2, 64
+    q = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    k = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    v = (rng.standard_normal((1, L, H, d)) + 30 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    for causal in (False, True):
+        ref = O.exact_attention(q, k, v, [L], None, causal)
+        m = v.astype(np.float64).mean(axis=1, keepdims=True)
+        sm = O.exact_attention(q, k, (v.astype(np.float64) - m), [L], None, causal) + m
+        np.testing.assert_allclose(sm, ref, rtol=0, atol=1e-12)
+
+
+def test_smooth_v_constant_channels_give_the_mean_exactly():
+    rng = np.random.default_rng(22)
+    L, H, d = 80, 2, 64
+    q = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    k = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    row = rng.standard_normal((1, 1, H, d)).astype(np.float16)
+    v = np.broadcast_to(row, (1, L, H, d)).copy()
+    for causal in (False, True):
+        o, qd = O.sage_attn(q, k, v, [L], None, causal, 64, 64, pv_fp8=True, smooth_v=True)
+        assert not qd["v8"].any() and not qd["sv"].any()
+        np.testing.assert_array_equal(qd["vm"][0], row[0, 0].astype(np.float32))
+        np.testing.assert_array_equal(o, np.broadcast_to(row.astype(np.float64), o.shape))
+
+
+def test_smooth_v_helps_channels_with_an_offset():
+    # V with a large per-channel offset: plain E4M3 spends its 3 mantissa bits on
+    # the offset, smoothed V on the variation around it
+    rng = np.random.default_rng(23)
+    L, H, d = 256, 2, 64
+    q = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    k = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    v = (rng.standard_normal((1, L, H, d)) + 40 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    ref = O.exact_attention(q, k, v, [L], None, False)
+    o_plain, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64, pv_fp8=True)
+    o_smooth, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64, pv_fp8=True, smooth_v=True)
+    dev = lambda o: o - ref.mean(axis=1, keepdims=True)  # noqa: E731  (compare the part beyond the offset)
+    c_plain = cos(dev(o_plain), dev(ref))
+    c_smooth = cos(dev(o_smooth), dev(ref))
+    assert c_smooth >= 0.99
+    assert c_smooth > c_plain + 0.01
+    assert np.abs(o_smooth - ref).max() < 0.5 * np.abs(o_plain - ref).max()
