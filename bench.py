@@ -280,6 +280,7 @@ def extra_workloads(sage, torch, dev):
     g = torch.Generator(device=dev)
     cases = [("long causal B1 H32 N32768 d128", synth.LONG, True, 0, None),
              ("fp8-PV B4 H16 N8192 d128", synth.FP8, False, 1, None),
+             ("fp8-PV smooth-V B4 H16 N8192 d128", synth.FP8, False, 2, None),
              ("fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, None),
              ("video B2 H24 N16384 d64", synth.VIDEO, False, 0, None),
              ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen")]
@@ -303,7 +304,7 @@ def extra_workloads(sage, torch, dev):
         k = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) + bias).half()
         v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
         qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
-        vv, sv = (sage.quantize_v_fp8(v, **kw) if mode == 1 else (v, None))
+        vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
         out = torch.empty_like(q)
 
         def run():

@@ -10,6 +10,8 @@
  *   [SA2] "4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级" --
  *         section 即插即用举例 (input Q, K, V; output O) and section 技术方案
  *         item 4 (P and V quantised to FP8 E4M3).
+ *         The same page, after 技术方案: the optional smoothing of V (subtract
+ *         mean(V) per channel, add it back to the output).
  *   [GUIDE] "如何将SageAttention量化注意力机制集成到你的AI项目中获得2-5倍速度提升"
  *         -- section 针对不同AI任务的优化建议 (causal mode; varlen kernels).
  *
@@ -66,7 +68,10 @@ typedef enum {
   SAGE_ERR_HIP = -4
 } sage_status;
 
-typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1 } sage_pv_mode;
+/* P.V precision: fp16 P and V; E4M3 P and V; E4M3 P and smoothed V (V minus
+ * its per-channel mean, the mean added to O: the optional V smoothing the
+ * [SA2] page describes after 技术方案). */
+typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8 = 1, SAGE_PV_FP8_SMOOTH_V = 2 } sage_pv_mode;
 
 typedef struct {
   int64_t s, h, n;
@@ -85,7 +90,8 @@ typedef struct {
 
 /* Bytes of workspace sage_attn and sage_quantize need for this problem
  * (sage_attn: int8 Q/K, their scales, mean(K), column-sum partials and, for
- * SAGE_PV_FP8, the E4M3 V and its scales; sage_quantize: the column-sum
+ * the FP8 modes, the E4M3 V, its scales (and means and column statistics
+ * for SAGE_PV_FP8_SMOOTH_V); sage_quantize: the column-sum
  * partials only).  Writes *bytes; returns SAGE_OK or SAGE_ERR_INVALID_ARG. */
 int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes);
 int sage_quantize_workspace_bytes(const sage_problem* p, size_t* bytes);
@@ -111,6 +117,19 @@ int sage_quantize(const sage_problem* p,
 int sage_quantize_v_fp8(const sage_problem* p, const void* V, sage_strides vs,
                         uint8_t* v8, sage_strides v8s, float* v_scale, void* stream);
 
+/* Smoothed FP8 E4M3 V for pv_mode SAGE_PV_FP8_SMOOTH_V ([SA2], V smoothing):
+ *   v_mean[s][h][c] = fp32( (sum over the sequence's tokens of V, exact) / L )
+ *   V' = fp32(V - v_mean); v_scale = fp32(max |V'| / 448) per channel;
+ *   v8 = E4M3(fp32(V' / v_scale)) (a constant channel: scale 0, codes 0).
+ * v_scale_mean holds 2 * nseq*heads*head_dim floats: v_scale [nseq][heads][head_dim]
+ * followed by v_mean in the same layout.  `workspace` holds
+ * sage_quantize_v_fp8_smooth_workspace_bytes() bytes of scratch (column
+ * statistics per chunk of tokens). */
+int sage_quantize_v_fp8_smooth_workspace_bytes(const sage_problem* p, size_t* bytes);
+int sage_quantize_v_fp8_smooth(const sage_problem* p, const void* V, sage_strides vs,
+                               uint8_t* v8, sage_strides v8s, float* v_scale_mean,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Fused attention over already-quantised inputs ([SA] 技术方案; [SA2] 即插即用举例):
  *   S = (q8 . k8^T) * q_scale[block(i)] * k_scale[block(j)]   (INT32 accumulation)
  *   keys of other sequences never count; causal keeps key j <= query i;
@@ -118,16 +137,20 @@ int sage_quantize_v_fp8(const sage_problem* p, const void* V, sage_strides vs,
  *   fp32 accumulation (pv_mode SAGE_PV_FP16, V fp16, v_scale unused) or on
  *   FP8 MFMA with P as E4M3(448 * 2^(S log2e - m)), m the running row maximum
  *   rounded up to an integer, and V = v8 with per-channel v_scale applied in
- *   the epilogue (pv_mode SAGE_PV_FP8).  O is written as fp16 with strides os;
- *   rows of a sequence of length 0 are not written. */
+ *   the epilogue (pv_mode SAGE_PV_FP8).  pv_mode SAGE_PV_FP8_SMOOTH_V: V = v8
+ *   of the smoothed V and v_scale points to the scales followed by the means
+ *   (as written by sage_quantize_v_fp8_smooth); the epilogue adds the mean,
+ *   exact since every row of softmax(S) sums to 1.  O is written as fp16 with
+ *   strides os; rows of a sequence of length 0 are not written. */
 int sage_attn_quantized(const sage_problem* p,
                         const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
                         const float* q_scale, const float* k_scale,
                         const void* V, sage_strides vs, const float* v_scale,
                         void* out, sage_strides os, int causal, int pv_mode, void* stream);
 
-/* The whole forward pass: sage_quantize (+ sage_quantize_v_fp8 in FP8 mode)
- * into the workspace, then sage_attn_quantized.  O = softmax(Q K^T * sm_scale) V
+/* The whole forward pass: sage_quantize (+ sage_quantize_v_fp8 or
+ * sage_quantize_v_fp8_smooth in the FP8 modes) into the workspace, then
+ * sage_attn_quantized.  O = softmax(Q K^T * sm_scale) V
  * computed as described above.  `workspace` holds sage_workspace_bytes() bytes. */
 int sage_attn(const sage_problem* p,
               const void* Q, sage_strides qs, const void* K, sage_strides ks,

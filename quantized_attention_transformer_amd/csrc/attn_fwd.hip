@@ -817,7 +817,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * q + e;
           f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
-          if constexpr (FP8) f[e] *= a.v_scale[sh * D + cc + e];
+          if constexpr (FP8) {
+            f[e] *= a.v_scale[sh * D + cc + e];
+            if (a.v_mean) f[e] += a.v_mean[sh * D + cc + e];  // smoothed V: P (V - mean) + mean
+          }
         }
         const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
         *reinterpret_cast<v4h*>(orow + cc) = hv;

@@ -384,10 +384,13 @@ __global__ void k_v_scale(float* __restrict__ sv, int64_t n) {
   if (i < n) sv[i] = sv[i] / 448.0f;
 }
 
+// grid (nchunk, heads, nseq): E4M3 codes of V (vmean != nullptr: of V' =
+// fp32(V - vmean), the smoothed V) with the per-channel scales sv.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict__ V, Str vs,
                                                        const int32_t* __restrict__ cu, int max_seqlen,
-                                                       const float* __restrict__ sv, uint8_t* __restrict__ v8,
+                                                       const float* __restrict__ sv,
+                                                       const float* __restrict__ vmean, uint8_t* __restrict__ v8,
                                                        Str v8s) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
   const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
@@ -398,21 +401,111 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const _Float16* src = V + seq_head_base(cu, vs, s, h) + cg * 8;
   uint8_t* dst = v8 + seq_head_base(cu, v8s, s, h) + cg * 8;
-  float scale[8];
+  float scale[8], mean[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) scale[i] = sv[((int64_t)s * H + h) * D + cg * 8 + i];
+  for (int i = 0; i < 8; ++i) {
+    scale[i] = sv[((int64_t)s * H + h) * D + cg * 8 + i];
+    mean[i] = vmean ? vmean[((int64_t)s * H + h) * D + cg * 8 + i] : 0.0f;
+  }
 #pragma unroll 2
   for (int n = n0 + r; n < n1; n += RPP) {
     H8 x = load_h8(src + (int64_t)n * vs.n);
     float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = scale[i] > 0.0f ? (float)x.v[i] / scale[i] : 0.0f;
+    for (int i = 0; i < 8; ++i) y[i] = scale[i] > 0.0f ? ((float)x.v[i] - mean[i]) / scale[i] : 0.0f;
     uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
     uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
     *reinterpret_cast<uint2*>(dst + (int64_t)n * v8s.n) = make_uint2(w0, w1);
   }
+}
+
+// ---------------------------------------------------------------- smoothed E4M3 V
+// Smooth V (the optional V smoothing described after 技术方案 on the
+// SageAttention2 page): mean(V) per channel as for K (exact fp64 sums, one
+// fp64 divide, fp32), V' = fp32(V - mean), then the per-channel E4M3 scale
+// of V'.  x -> fp32(x - mean) is monotone, so max|V'| of a channel comes from
+// its fp16 maximum and minimum.
+
+// grid (nchunk, heads, nseq), kThreads: per chunk of kColChunk tokens and
+// channel, the exact fp64 sum and the fp16 maximum and minimum (as float).
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restrict__ V, Str vs,
+                                                          const int32_t* __restrict__ cu, int max_seqlen, int nchunk,
+                                                          double* __restrict__ psum, float* __restrict__ pmax,
+                                                          float* __restrict__ pmin) {
+  constexpr int TPR = D / 8, RPP = kThreads / TPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = chunk * kColChunk;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + kColChunk);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
+  double acc[8] = {};
+  Extremes ex;
+#pragma unroll 4
+  for (int n = n0 + r; n < n1; n += RPP) {
+    const H8 x = load_h8(base + (int64_t)n * vs.n);
+    ex.add(x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+  }
+  __shared__ double rsum[RPP][D];
+  __shared__ float rmax[RPP][D], rmin[RPP][D];
+  const bool any = n0 + r < n1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    rsum[r][cg * 8 + i] = acc[i];
+    rmax[r][cg * 8 + i] = any ? (float)ex.hi[i >> 1][i & 1] : -INFINITY;
+    rmin[r][cg * 8 + i] = any ? (float)ex.lo[i >> 1][i & 1] : INFINITY;
+  }
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+    float hi = -INFINITY, lo = INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) {
+      t += rsum[i][tid];
+      hi = fmaxf(hi, rmax[i][tid]);
+      lo = fminf(lo, rmin[i][tid]);
+    }
+    const int64_t o = (((int64_t)s * H + h) * nchunk + chunk) * D + tid;
+    psum[o] = t;
+    pmax[o] = hi;
+    pmin[o] = lo;
+  }
+}
+
+// grid (heads, nseq), D threads: mean = fp32(sum / L); scale = fp32(max(|fp32(max -
+// mean)|, |fp32(min - mean)|) / 448) per channel (0 for an empty sequence).
+template <int D>
+__global__ __launch_bounds__(D) void k_v_finalize(const double* __restrict__ psum, const float* __restrict__ pmax,
+                                                  const float* __restrict__ pmin, const int32_t* __restrict__ cu,
+                                                  int max_seqlen, int nchunk, float* __restrict__ sv,
+                                                  float* __restrict__ vmean) {
+  const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int64_t sh = (int64_t)s * H + h;
+  if (L <= 0) {
+    sv[sh * D + c] = 0.0f;
+    vmean[sh * D + c] = 0.0f;
+    return;
+  }
+  const int nc = (L + kColChunk - 1) / kColChunk;
+  double t = 0.0;
+  float hi = -INFINITY, lo = INFINITY;
+  for (int k = 0; k < nc; ++k) {
+    const int64_t o = (sh * nchunk + k) * D + c;
+    t += psum[o];
+    hi = fmaxf(hi, pmax[o]);
+    lo = fminf(lo, pmin[o]);
+  }
+  const float mean = (float)(t / (double)L);
+  const float a = fmaxf(fabsf(hi - mean), fabsf(lo - mean));
+  sv[sh * D + c] = a / 448.0f;
+  vmean[sh * D + c] = mean;
 }
 
 }  // namespace
@@ -476,11 +569,25 @@ hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, uint8_t* v8, Str v8s,
-                          hipStream_t st) {
+hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, const float* v_mean,
+                          uint8_t* v8, Str v8s, hipStream_t st) {
   dim3 grid(p.nchunk, p.heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_v<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, v_scale, v8, v8s));
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, v_scale, v_mean, v8,
+                                                 v8s));
+  return hipGetLastError();
+}
+
+hipError_t launch_v_smooth_stats(const Problem& p, const void* V, Str vs, double* psum, float* pmax, float* pmin,
+                                 float* v_scale, float* v_mean, hipStream_t st) {
+  dim3 grid(p.nchunk, p.heads, p.nseq);
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colstats<D>), grid, dim3(kThreads), 0, st,
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.nchunk, psum, pmax,
+                                                 pmin));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_finalize<D>), dim3(p.heads, p.nseq), dim3(D), 0, st, psum,
+                                                 pmax, pmin, p.cu, p.max_seqlen, p.nchunk, v_scale, v_mean));
   return hipGetLastError();
 }
 

@@ -97,9 +97,27 @@ int64_t tokens(const sage_problem* p) {
 // are stored head-major: dense [nseq][heads][max_seqlen][d], packed
 // [heads][total_tokens][d].
 struct WsLayout {
-  size_t q8, k8, sq, sk, km, colsum, v8, sv, total;
+  size_t q8, k8, sq, sk, km, colsum, v8, sv, vpsum, vpmax, vpmin, total;
   sage_strides s8;
 };
+
+bool valid_pv_mode(int m) { return m == SAGE_PV_FP16 || m == SAGE_PV_FP8 || m == SAGE_PV_FP8_SMOOTH_V; }
+
+// Partials of the smoothed-V statistics (sum, max, min per chunk and channel).
+struct VSmoothWs {
+  size_t psum, pmax, pmin, total;
+};
+
+VSmoothWs v_smooth_ws(const sage_problem* p, size_t base) {
+  const sage::Problem q = to_internal(p);
+  const size_t n = (size_t)p->nseq * p->heads * q.nchunk * p->head_dim;
+  VSmoothWs w{};
+  w.psum = base;
+  w.pmax = w.psum + align_up(n * 8);
+  w.pmin = w.pmax + align_up(n * 4);
+  w.total = w.pmin + align_up(n * 4) - base;
+  return w;
+}
 
 WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   const sage::Problem q = to_internal(p);
@@ -118,9 +136,17 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   w.sk = take((size_t)p->nseq * H * q.nbk * 4);
   w.km = take((size_t)p->nseq * H * d * 4);
   w.colsum = take((size_t)p->nseq * H * q.nbq * d * 8);
-  if (pv_mode == SAGE_PV_FP8) {
+  if (pv_mode == SAGE_PV_FP8 || pv_mode == SAGE_PV_FP8_SMOOTH_V) {
     w.v8 = take((size_t)(T * H * d));
-    w.sv = take((size_t)p->nseq * H * d * 4);
+    // scales (then, smoothed V: the means)
+    w.sv = take((size_t)p->nseq * H * d * 4 * (pv_mode == SAGE_PV_FP8_SMOOTH_V ? 2 : 1));
+  }
+  if (pv_mode == SAGE_PV_FP8_SMOOTH_V) {
+    const VSmoothWs v = v_smooth_ws(p, off);
+    w.vpsum = v.psum;
+    w.vpmax = v.pmax;
+    w.vpmin = v.pmin;
+    off += v.total;
   }
   w.total = off;
   if (p->cu_seqlens)
@@ -155,7 +181,21 @@ int run_quantize_v(const sage_problem* p, const void* V, sage_strides vs, uint8_
   hipError_t e;
   if ((e = sage::launch_v_colmax(q, V, S(vs), v_scale, st)) != hipSuccess) return hip_fail(e, "v_colmax launch");
   if ((e = sage::launch_v_scale(q, v_scale, st)) != hipSuccess) return hip_fail(e, "v_scale launch");
-  if ((e = sage::launch_quant_v(q, V, S(vs), v_scale, v8, S(v8s), st)) != hipSuccess)
+  if ((e = sage::launch_quant_v(q, V, S(vs), v_scale, nullptr, v8, S(v8s), st)) != hipSuccess)
+    return hip_fail(e, "quant_v launch");
+  return SAGE_OK;
+}
+
+// v_scale_mean: nseq*heads*head_dim scales, then as many means.
+int run_quantize_v_smooth(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
+                          float* v_scale_mean, char* ws, const VSmoothWs& w, hipStream_t st) {
+  const sage::Problem q = to_internal(p);
+  float* const vmean = v_scale_mean + (size_t)p->nseq * p->heads * p->head_dim;
+  hipError_t e;
+  if ((e = sage::launch_v_smooth_stats(q, V, S(vs), (double*)(ws + w.psum), (float*)(ws + w.pmax),
+                                       (float*)(ws + w.pmin), v_scale_mean, vmean, st)) != hipSuccess)
+    return hip_fail(e, "v smooth stats launch");
+  if ((e = sage::launch_quant_v(q, V, S(vs), v_scale_mean, vmean, v8, S(v8s), st)) != hipSuccess)
     return hip_fail(e, "quant_v launch");
   return SAGE_OK;
 }
@@ -169,7 +209,7 @@ const char* sage_last_error(void) { return g_last_error.c_str(); }
 int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes) {
   int rc = check_problem(p);
   if (rc) return rc;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = ws_layout(p, pv_mode).total;
   return SAGE_OK;
@@ -200,6 +240,28 @@ int sage_quantize(const sage_problem* p, const void* Q, sage_strides qs, const v
                       (hipStream_t)stream);
 }
 
+int sage_quantize_v_fp8_smooth_workspace_bytes(const sage_problem* p, size_t* bytes) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = v_smooth_ws(p, 0).total;
+  return SAGE_OK;
+}
+
+int sage_quantize_v_fp8_smooth(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
+                               float* v_scale_mean, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("v8", v8, v8s, 16, p))) return rc;
+  if (!v_scale_mean) return fail(SAGE_ERR_INVALID_ARG, "v_scale_mean is NULL");
+  const VSmoothWs w = v_smooth_ws(p, 0);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, w.total);
+  if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return run_quantize_v_smooth(p, V, vs, v8, v8s, v_scale_mean, (char*)workspace, w, (hipStream_t)stream);
+}
+
 int sage_quantize_v_fp8(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
                         float* v_scale, void* stream) {
   int rc = check_problem(p);
@@ -215,15 +277,17 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
                         const float* v_scale, void* out, sage_strides os, int causal, int pv_mode, void* stream) {
   int rc = check_problem(p);
   if (rc) return rc;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
-  const bool fp8 = pv_mode == SAGE_PV_FP8;
+  const bool fp8 = pv_mode != SAGE_PV_FP16;
   if ((rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)) ||
       (rc = check_tensor("V", V, vs, fp8 ? 16 : 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
     return rc;
   if (!q_scale || !k_scale || (fp8 && !v_scale)) return fail(SAGE_ERR_INVALID_ARG, "scales must not be NULL");
   if ((rc = check_row_span("k8", k8s, 1, p)) || (rc = check_row_span("V", vs, fp8 ? 1 : 2, p))) return rc;
-  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr};
+  const float* v_mean =
+      pv_mode == SAGE_PV_FP8_SMOOTH_V ? v_scale + (size_t)p->nseq * p->heads * p->head_dim : nullptr;
+  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr, v_mean};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;
@@ -234,7 +298,7 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
               size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
   if (rc) return rc;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
+  if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
       (rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
@@ -256,15 +320,23 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   const void* vin = V;
   sage_strides vin_s = vs;
   const float* sv = nullptr;
+  const float* vmean = nullptr;
   if (pv_mode == SAGE_PV_FP8) {
     if ((rc = run_quantize_v(p, V, vs, (uint8_t*)(ws + w.v8), w.s8, (float*)(ws + w.sv), st)))
       return rc;
+  } else if (pv_mode == SAGE_PV_FP8_SMOOTH_V) {
+    const VSmoothWs vw{w.vpsum, w.vpmax, w.vpmin, 0};
+    if ((rc = run_quantize_v_smooth(p, V, vs, (uint8_t*)(ws + w.v8), w.s8, (float*)(ws + w.sv), ws, vw, st)))
+      return rc;
+    vmean = (const float*)(ws + w.sv) + (size_t)p->nseq * p->heads * p->head_dim;
+  }
+  if (pv_mode != SAGE_PV_FP16) {
     vin = ws + w.v8;
     vin_s = w.s8;
     sv = (const float*)(ws + w.sv);
   }
-  sage::AttnArgs a{q8, S(w.s8), k8, S(w.s8), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr};
-  hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode == SAGE_PV_FP8, st);
+  sage::AttnArgs a{q8, S(w.s8), k8, S(w.s8), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean};
+  hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode != SAGE_PV_FP16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;
 }
@@ -280,8 +352,8 @@ int sage_debug_qk_i32(const sage_problem* p, const int8_t* q8, sage_strides q8s,
   if (!s_out || !aligned16(s_out)) return fail(SAGE_ERR_INVALID_ARG, "s_out must be non-NULL and 16-byte aligned");
   if (p->max_seqlen % 4) return fail(SAGE_ERR_UNSUPPORTED, "sage_debug_qk_i32 needs max_seqlen % 4 == 0");
   // scales are not read on the integer path
-  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), nullptr, nullptr, nullptr, sage::Str{0, 0, 0}, nullptr, nullptr,
-                   sage::Str{0, 0, 0}, s_out};
+  sage::AttnArgs a{q8,      S(q8s),  k8,      S(k8s),  nullptr, nullptr, nullptr, sage::Str{0, 0, 0},
+                   nullptr, nullptr, sage::Str{0, 0, 0}, s_out, nullptr};
   hipError_t e = sage::launch_attn(to_internal(p), a, false, false, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "debug qk launch");
   return SAGE_OK;

@@ -41,8 +41,14 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
 // v_scale = max|V| / 448 per (sequence, head, channel): zero fill, atomic column max, divide in place.
 hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* v_scale, hipStream_t st);
 hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st);
-hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, uint8_t* v8, Str v8s,
-                          hipStream_t st);
+// E4M3 codes of V (v_mean != nullptr: of fp32(V - v_mean)) with the per-channel v_scale.
+hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, const float* v_mean,
+                          uint8_t* v8, Str v8s, hipStream_t st);
+// Smoothed V: per chunk of kColChunk tokens the exact fp64 column sums and the fp16 column
+// max/min (psum, pmax, pmin: nseq*heads*nchunk*head_dim each), then per (sequence, head,
+// channel) v_mean = fp32(sum / L) and v_scale = max|fp32(V - v_mean)| / 448.
+hipError_t launch_v_smooth_stats(const Problem& p, const void* V, Str vs, double* psum, float* pmax, float* pmin,
+                                 float* v_scale, float* v_mean, hipStream_t st);
 
 // ---- fused attention (attn_fwd.hip) ----
 struct AttnArgs {
@@ -58,6 +64,7 @@ struct AttnArgs {
   void* out;  // fp16
   Str os;
   int32_t* dump;  // debug i32 scores or nullptr
+  const float* v_mean;  // FP8 with smoothed V: per-channel mean added to O, else nullptr
 };
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
 // One FP8 P.V MFMA on given operands (debug; one wave).

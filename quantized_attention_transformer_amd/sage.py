@@ -23,8 +23,10 @@ _lib = None
 
 SAGE_PV_FP16 = 0
 SAGE_PV_FP8 = 1
+SAGE_PV_FP8_SMOOTH_V = 2
 
 EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quantize", "sage_quantize_v_fp8",
+            "sage_quantize_v_fp8_smooth_workspace_bytes", "sage_quantize_v_fp8_smooth",
             "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma", "sage_last_error")
 
 
@@ -57,6 +59,8 @@ def lib():
         L.sage_quantize_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
         L.sage_quantize.argtypes = [P, vp, S, vp, S, f32, vp, S, vp, S, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_v_fp8.argtypes = [P, vp, S, vp, S, vp, vp]
+        L.sage_quantize_v_fp8_smooth_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+        L.sage_quantize_v_fp8_smooth.argtypes = [P, vp, S, vp, S, vp, vp, sz, vp]
         L.sage_attn_quantized.argtypes = [P, vp, S, vp, S, vp, vp, vp, S, vp, vp, S, i32, i32, vp]
         L.sage_attn.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp, sz, vp]
         L.sage_debug_qk_i32.argtypes = [P, vp, S, vp, S, vp, vp]
@@ -149,10 +153,22 @@ def quantize(q, k, *, sm_scale: Optional[float] = None, layout="bnhd", cu_seqlen
     return dict(q8=q8, k8=k8, q_scale=sq, k_scale=sk, k_mean=km)
 
 
-def quantize_v_fp8(v, *, layout="bnhd", cu_seqlens=None, max_seqlen=None):
-    """sage_quantize_v_fp8: returns (v8 uint8 E4M3 codes in v's shape, v_scale [nseq, H, d])."""
+def quantize_v_fp8(v, *, layout="bnhd", cu_seqlens=None, max_seqlen=None, smooth=False):
+    """sage_quantize_v_fp8: returns (v8 uint8 E4M3 codes in v's shape, v_scale [nseq, H, d]).
+    smooth=True: sage_quantize_v_fp8_smooth, returns (v8 of the smoothed V, v_scale_mean
+    [2, nseq, H, d]: the scales, then the means), for pv_mode SAGE_PV_FP8_SMOOTH_V."""
     prob = make_problem(v, layout, cu_seqlens, max_seqlen)
     v8 = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    if smooth:
+        n = ctypes.c_size_t(0)
+        _check("sage_quantize_v_fp8_smooth_workspace_bytes",
+               lib().sage_quantize_v_fp8_smooth_workspace_bytes(ctypes.byref(prob), ctypes.byref(n)))
+        ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=v.device)
+        svm = torch.zeros((2, prob.nseq, prob.heads, prob.head_dim), dtype=torch.float32, device=v.device)
+        rc = lib().sage_quantize_v_fp8_smooth(ctypes.byref(prob), _ptr(v), strides_of(v, layout), _ptr(v8),
+                                              strides_of(v8, layout), _ptr(svm), _ptr(ws), ws.numel(), _stream())
+        _check("sage_quantize_v_fp8_smooth", rc)
+        return v8, svm
     sv = torch.zeros((prob.nseq, prob.heads, prob.head_dim), dtype=torch.float32, device=v.device)
     rc = lib().sage_quantize_v_fp8(ctypes.byref(prob), _ptr(v), strides_of(v, layout), _ptr(v8),
                                    strides_of(v8, layout), _ptr(sv), _stream())

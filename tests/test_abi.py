@@ -57,6 +57,13 @@ def test_workspace_bytes_layout():
     m = ctypes.c_size_t(0)
     assert sage.lib().sage_quantize_workspace_bytes(ctypes.byref(_prob()), ctypes.byref(m)) == 0
     assert m.value == 4096
+    # smoothed V: per chunk of 512 tokens (1 here) and channel an fp64 sum and fp32
+    # max and min (2 heads x 64 channels), and the scales followed by the means
+    sv = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_v_fp8_smooth_workspace_bytes(ctypes.byref(_prob()), ctypes.byref(sv)) == 0
+    assert sv.value == 1024 + 512 + 512
+    rcs, ns = _ws(_prob(), 2)
+    assert rcs == 0 and ns == n + 32768 + 2 * 512 + sv.value
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -79,6 +86,25 @@ def test_null_problem_and_bad_mode():
     n = ctypes.c_size_t(0)
     assert sage.lib().sage_workspace_bytes(None, 0, ctypes.byref(n)) == -1
     assert sage.lib().sage_workspace_bytes(ctypes.byref(_prob()), 7, ctypes.byref(n)) == -1
+    assert sage.lib().sage_workspace_bytes(ctypes.byref(_prob()), 3, ctypes.byref(n)) == -1
+
+
+def test_smooth_v_rejects_small_workspace_and_null_output():
+    p = _prob()
+    need = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_v_fp8_smooth_workspace_bytes(ctypes.byref(p), ctypes.byref(need)) == 0
+    st = _strides()
+    r = sage.lib().sage_quantize_v_fp8_smooth(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, FAKE, need.value - 1, None)
+    assert r == -3 and "workspace" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_quantize_v_fp8_smooth(ctypes.byref(p), FAKE, st, FAKE, st, None, FAKE, need.value, None)
+    assert r == -1 and "v_scale_mean" in sage.lib().sage_last_error().decode()
+
+
+def test_debug_fp8_mfma_rejects_bad_scales():
+    r = sage.lib().sage_debug_fp8_mfma(FAKE, FAKE, FAKE, 255, 127, FAKE, None)
+    assert r == -1 and "E8M0" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_debug_fp8_mfma(None, FAKE, FAKE, 127, 127, FAKE, None)
+    assert r == -1
 
 
 FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced: validation fails first
