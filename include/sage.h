@@ -9,7 +9,8 @@
  *         P.V kept in FP16 with an FP16 accumulator.
  *   [SA2] "4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级" --
  *         section 即插即用举例 (input Q, K, V; output O) and section 技术方案
- *         item 4 (P and V quantised to FP8 E4M3).
+ *         item 2 (quantisation finer than per block) and item 4 (P and V
+ *         quantised to FP8 E4M3).
  *         The same page, after 技术方案: the optional smoothing of V (subtract
  *         mean(V) per channel, add it back to the output).
  *   [GUIDE] "如何将SageAttention量化注意力机制集成到你的AI项目中获得2-5倍速度提升"
@@ -36,8 +37,11 @@
  *   sequence's last block are left unspecified.  k_mean and v_scale are
  *   [nseq][heads][head_dim] fp32, contiguous.
  * Blocks.  blk_q and blk_k: quantisation block lengths in tokens, multiples
- *   of 16 in [16, 256].  Blocks restart at each sequence's first token; the
- *   last block of a sequence holds its remaining tokens.
+ *   of 16 in [16, 256]; blk_q may also be 1, one Q scale per token (finer
+ *   than per-block, as [SA2] 技术方案 item 2 argues; in the fused kernel each
+ *   lane holds one query row, so a per-token scale costs nothing there).
+ *   Blocks restart at each sequence's first token; the last block of a
+ *   sequence holds its remaining tokens.
  * Ownership.  The caller allocates every buffer (device memory) including
  *   the workspace; the library allocates and frees nothing on the device and
  *   keeps no pointer after returning.

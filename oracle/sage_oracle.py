@@ -116,7 +116,8 @@ def quant_block(x: np.ndarray):
 def quant_rows(x: np.ndarray, blk: int):
     """Blocks of `blk` rows starting at the sequence's first token; the last
     block holds the remaining rows.  x: fp32 [L, d] -> (int8 [L, d], fp32
-    [ceil(L/blk)])."""
+    [ceil(L/blk)]).  blk = 1 is one scale per token, the finest of the
+    granularities finer than per-block that [SA2] 技术方案 item 2 argues for."""
     L = x.shape[0]
     nb = -(-L // blk)
     codes = np.zeros(x.shape, np.int8)

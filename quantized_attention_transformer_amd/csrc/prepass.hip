@@ -202,33 +202,63 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
   return scale;
 }
 
-// grid (2*nbq, heads, nseq), kQThreads: workgroup 2bi quantises Q block bi
-// (INT8 Q' = Q * sm_scale); workgroup 2bi+1 takes the fp64 column sums of K
-// over the same rows, one partial per Q block.
+// grid (nqw + nks, heads, nseq), kQThreads.  Workgroups x < nqw quantise Q
+// (INT8 Q' = Q * sm_scale): block x of blk_q rows, or for blk_q == 1 (one
+// scale per token) the RPP rows x*RPP .. x*RPP+RPP-1, TPR threads per row.
+// Workgroups x >= nqw take the fp64 column sums of K over the tokens of chunk
+// x - nqw (kKSumRows tokens), one partial per chunk.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
-    int max_seqlen, int blk_q, int nbq, float sm_scale, int8_t* __restrict__ q8, Str q8s, float* __restrict__ sq,
-    double* __restrict__ part) {
+    int max_seqlen, int blk_q, int nbq, int nqw, int nks, float sm_scale, int8_t* __restrict__ q8, Str q8s,
+    float* __restrict__ sq, double* __restrict__ part) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
-  const int bi = blockIdx.x >> 1, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int L = seq_len(cu, s, max_seqlen);
-  const int n0 = bi * blk_q;
-  if (n0 >= L) return;
-  const int n1 = min(L, n0 + blk_q);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const int64_t sh = (int64_t)s * H + h;
-  if ((blockIdx.x & 1) == 0) {
-    const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1,
-                                       [&](float v, int) { return v * sm_scale; },
+  auto scale_q = [&](float v, int) { return v * sm_scale; };
+  if (x < nqw && blk_q == 1) {
+    // one scale per token: absmax of the row = fp32(max |Q| * sm_scale) (monotone)
+    if (x * RPP >= L) return;
+    const int n = x * RPP + r;
+    const bool valid = n < L;
+    H8 row;
+    float a = 0.0f;
+    if (valid) {
+      row = load_h8(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf((float)row.v[i]));
+      a *= sm_scale;
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));  // the row's TPR lanes
+    if (valid) {
+      const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h) + (int64_t)n * q8s.n + cg * 8) =
+          a > 0.0f ? codes8(row, scale_q, scale, __builtin_amdgcn_rcpf(scale)) : make_uint2(0u, 0u);
+      if (cg == 0) sq[sh * nbq + n] = scale;
+    }
+    return;
+  }
+  if (x < nqw) {
+    const int n0 = x * blk_q;
+    if (n0 >= L) return;
+    const int n1 = min(L, n0 + blk_q);
+    const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, scale_q,
                                        q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n);
-    if (tid == 0) sq[sh * nbq + bi] = scale;
+    if (tid == 0) sq[sh * nbq + x] = scale;
     return;
   }
   // K column sums (exact in fp64, in any order)
+  const int ci = x - nqw;
+  const int n0 = ci * kKSumRows;
+  if (n0 >= L) return;
+  const int n1 = min(L, n0 + kKSumRows);
   const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
   double acc[8] = {};
-  if (n1 - n0 <= 128) {
+  static_assert(kKSumRows <= 128, "a chunk fits the register-cached rows");
+  {
     BlockRows<D> krows;
     krows.load(kb, ks.n, n0, n1);
 #pragma unroll
@@ -236,13 +266,6 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
       if (n0 + r + RPP * j < n1)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += (double)(float)krows.x[j].v[i];
-  } else {
-#pragma unroll 4
-    for (int n = n0 + r; n < n1; n += RPP) {
-      H8 x = load_h8(kb + (int64_t)n * ks.n);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
-    }
   }
   __shared__ double red[RPP][D];
 #pragma unroll
@@ -252,11 +275,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     double t = 0.0;
 #pragma unroll
     for (int i = 0; i < RPP; ++i) t += red[i][tid];
-    part[(sh * nbq + bi) * D + tid] = t;
+    part[(sh * nks + ci) * D + tid] = t;
   }
 }
 
-// Sum of the nb = ceil(L / blk_q) partials of channel c of (s, h), by the
+// Sum of the nb = ceil(L / kKSumRows) partials of channel c of (s, h), by the
 // kQThreads / D threads of c (16 independent loads per round), combined in LDS.
 template <int D>
 __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, int nb, int c, int g) {
@@ -286,11 +309,11 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
                                                              const int32_t* __restrict__ cu, int max_seqlen,
-                                                             int blk_q, int nbq, float* __restrict__ km) {
+                                                             int nks, float* __restrict__ km) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
   const int L = seq_len(cu, s, max_seqlen);
-  const int nb = (L + blk_q - 1) / blk_q;
-  const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nbq * D + c, nb, c, g);
+  const int nb = (L + kKSumRows - 1) / kKSumRows;
+  const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nks * D + c, nb, c, g);
   if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(sum / (double)L) : 0.0f;
 }
 
@@ -301,7 +324,7 @@ __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __res
 template <int D, bool FOLD>
 __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
                                                        const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
-                                                       int nbk, int blk_q, int nbq, const double* __restrict__ part,
+                                                       int nbk, int nks, const double* __restrict__ part,
                                                        float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
                                                        float* __restrict__ sk) {
   constexpr int TPR = D / 8;
@@ -320,7 +343,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
   if constexpr (FOLD) {
     __shared__ float kmean[D];
     const int c = threadIdx.x % D, g = threadIdx.x / D;
-    const double sum = sum_partials<D>(part + sh * nbq * D + c, (L + blk_q - 1) / blk_q, c, g);
+    const double sum = sum_partials<D>(part + sh * nks * D + c, (L + kKSumRows - 1) / kKSumRows, c, g);
     if (g == 0) {
       const float mv = (float)(sum / (double)L);
       kmean[c] = mv;
@@ -523,34 +546,37 @@ __global__ __launch_bounds__(D) void k_v_finalize(const double* __restrict__ psu
     }                                    \
   } while (0)
 
-// Heads with at most this many Q blocks fold the mean into k_quant_k.
+// Heads with at most this many K column-sum partials fold the mean into k_quant_k.
 constexpr int kFoldMaxBlocks = 64;
 
 hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st) {
-  dim3 grid(2 * p.nbq, p.heads, p.nseq);
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_q_colsum<D>), grid, dim3(kQThreads), 0, st,
-                                                 (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen,
-                                                 p.blk_q, p.nbq, sm_scale, q8, q8s, q_scale, partial));
+  SAGE_DISPATCH_D(p.head_dim, {
+    constexpr int RPP = kQThreads / (D / 8);  // rows per workgroup of the per-token path
+    const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
+    hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st,
+                       (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.nbq, nqw,
+                       p.nks, sm_scale, q8, q8s, q_scale, partial);
+  });
   return hipGetLastError();
 }
 
 hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
                           Str k8s, float* k_scale, hipStream_t st) {
   dim3 grid(p.nbk, p.heads, p.nseq);
-  if (p.nbq <= kFoldMaxBlocks) {
+  if (p.nks <= kFoldMaxBlocks) {
     SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
-                                                   (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
-                                                   p.nbq, partial, k_mean, k8, k8s, k_scale));
+                                                   (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
+                                                   partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st,
-                                                 partial, p.cu, p.max_seqlen, p.blk_q, p.nbq, k_mean));
+                                                 partial, p.cu, p.max_seqlen, p.nks, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
-                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.blk_q,
-                                                 p.nbq, partial, k_mean, k8, k8s, k_scale));
+                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
+                                                 partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
 }
 

@@ -42,10 +42,11 @@ int check_problem(const sage_problem* p) {
                 p->heads, p->max_seqlen);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
-  for (int b : {p->blk_q, p->blk_k})
-    if (b < 16 || b > 256 || b % 16 != 0)
-      return fail(SAGE_ERR_INVALID_ARG, "blk_q/blk_k (%d, %d) must be multiples of 16 in [16, 256]", p->blk_q,
-                  p->blk_k);
+  auto block_ok = [](int b) { return b >= 16 && b <= 256 && b % 16 == 0; };
+  if (!(block_ok(p->blk_q) || p->blk_q == 1) || !block_ok(p->blk_k))
+    return fail(SAGE_ERR_INVALID_ARG,
+                "blk_q/blk_k (%d, %d) must be multiples of 16 in [16, 256] (blk_q may also be 1: per token)",
+                p->blk_q, p->blk_k);
   if (p->cu_seqlens && p->total_tokens < 0) return fail(SAGE_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (p->heads > 65535 || p->nseq > 65535) return fail(SAGE_ERR_UNSUPPORTED, "heads and nseq must be <= 65535");
   return SAGE_OK;
@@ -65,6 +66,7 @@ sage::Problem to_internal(const sage_problem* p) {
   q.nbq = (int)cdiv(p->max_seqlen, p->blk_q);
   q.nbk = (int)cdiv(p->max_seqlen, p->blk_k);
   q.nchunk = (int)cdiv(p->max_seqlen, sage::kColChunk);
+  q.nks = (int)cdiv(p->max_seqlen, sage::kKSumRows);
   return q;
 }
 
@@ -135,7 +137,7 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   w.sq = take((size_t)p->nseq * H * q.nbq * 4);
   w.sk = take((size_t)p->nseq * H * q.nbk * 4);
   w.km = take((size_t)p->nseq * H * d * 4);
-  w.colsum = take((size_t)p->nseq * H * q.nbq * d * 8);
+  w.colsum = take((size_t)p->nseq * H * q.nks * d * 8);
   if (pv_mode == SAGE_PV_FP8 || pv_mode == SAGE_PV_FP8_SMOOTH_V) {
     w.v8 = take((size_t)(T * H * d));
     // scales (then, smoothed V: the means)
@@ -158,7 +160,7 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
 
 size_t quantize_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
-  return align_up((size_t)p->nseq * p->heads * q.nbq * p->head_dim * 8);
+  return align_up((size_t)p->nseq * p->heads * q.nks * p->head_dim * 8);
 }
 
 int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,

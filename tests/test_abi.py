@@ -48,15 +48,18 @@ def _ws(p, mode=0):
 def test_workspace_bytes_layout():
     rc, n = _ws(_prob())
     assert rc == 0
-    # int8 Q and K (2 x 32 KiB), scales, mean, fp64 column-sum partials (one per Q block:
-    # 2 heads x 4 blocks x 64 channels x 8 bytes); 256-byte aligned regions
-    assert n == 2 * 32768 + 256 + 256 + 512 + 4096
+    # int8 Q and K (2 x 32 KiB), scales, mean, fp64 K column-sum partials (one per 128
+    # tokens: 2 heads x 2 chunks x 64 channels x 8 bytes); 256-byte aligned regions
+    assert n == 2 * 32768 + 256 + 256 + 512 + 2048
     rc8, n8 = _ws(_prob(), 1)
     assert rc8 == 0 and n8 == n + 32768 + 512
     # quantize-only workspace: the column-sum partials
     m = ctypes.c_size_t(0)
     assert sage.lib().sage_quantize_workspace_bytes(ctypes.byref(_prob()), ctypes.byref(m)) == 0
-    assert m.value == 4096
+    assert m.value == 2048
+    # one Q scale per token: 2 heads x 256 scales
+    rc1, n1 = _ws(_prob(blk_q=1))
+    assert rc1 == 0 and n1 == n - 256 + 2048
     # smoothed V: per chunk of 512 tokens (1 here) and channel an fp64 sum and fp32
     # max and min (2 heads x 64 channels), and the scales followed by the means
     sv = ctypes.c_size_t(0)
@@ -70,6 +73,8 @@ def test_workspace_bytes_layout():
     (dict(head_dim=96), -2),
     (dict(head_dim=0), -2),
     (dict(blk_q=24), -1),
+    (dict(blk_k=1), -1),
+    (dict(blk_q=2), -1),
     (dict(blk_k=512), -1),
     (dict(blk_k=0), -1),
     (dict(heads=0), -1),

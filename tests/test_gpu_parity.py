@@ -97,15 +97,29 @@ def test_e4m3_convert_matches_oracle_on_every_code_and_tie():
 QUANT_CASES = [synth.TINY, synth.TEXT, synth.VIDEO, synth.VARLEN, synth.LONG, synth.FP8]
 
 
+PER_TOKEN_CASES = [("text-full-blk1", synth.TEXT, {}), ("varlen-ragged-blk1", synth.VARLEN,
+                                                          dict(seqlens=[37, 0, 130, 64, 1, 300], heads=3)),
+                   ("tiny-d64-blk1", synth.TINY, {})]
+
+
 @pytest.mark.parametrize("wl", QUANT_CASES, ids=lambda w: w.name)
 def test_quantize_bitexact_full_size(wl):
-    inp = synth.generate(wl)
-    print(f"[{wl.name}] shapes q{inp.q.shape} seqlens={list(inp.seqlens)}", flush=True)
-    g = S().quantize(dev(inp.q), dev(inp.k), blk_q=wl.blk_q, blk_k=wl.blk_k, **gpu_kwargs(inp))
-    ref = O.quantize_qk(inp.q, inp.k, inp.seqlens, inp.cu_seqlens, wl.blk_q, wl.blk_k)
+    check_quantize(wl.name, synth.generate(wl), wl.blk_q, wl.blk_k)
+
+
+@pytest.mark.parametrize("name,wl,kw", PER_TOKEN_CASES, ids=[c[0] for c in PER_TOKEN_CASES])
+def test_quantize_per_token_q_bitexact(name, wl, kw):
+    # blk_q = 1: one Q scale per token
+    check_quantize(name, synth.generate(wl, **kw), 1, wl.blk_k)
+
+
+def check_quantize(name, inp, blk_q, blk_k):
+    print(f"[{name}] shapes q{inp.q.shape} seqlens={list(inp.seqlens)} blocks {blk_q}/{blk_k}", flush=True)
+    g = S().quantize(dev(inp.q), dev(inp.k), blk_q=blk_q, blk_k=blk_k, **gpu_kwargs(inp))
+    ref = O.quantize_qk(inp.q, inp.k, inp.seqlens, inp.cu_seqlens, blk_q, blk_k)
     np.testing.assert_array_equal(host(g["k_mean"]), ref["km"])
-    mq = valid_scale_mask(inp.seqlens, ref["sq"].shape[2], wl.blk_q)
-    mk = valid_scale_mask(inp.seqlens, ref["sk"].shape[2], wl.blk_k)
+    mq = valid_scale_mask(inp.seqlens, ref["sq"].shape[2], blk_q)
+    mk = valid_scale_mask(inp.seqlens, ref["sk"].shape[2], blk_k)
     np.testing.assert_array_equal(host(g["q_scale"])[mq[:, None, :].repeat(inp.q.shape[-2], 1)],
                                   ref["sq"][mq[:, None, :].repeat(inp.q.shape[-2], 1)])
     np.testing.assert_array_equal(host(g["k_scale"])[mk[:, None, :].repeat(inp.q.shape[-2], 1)],
@@ -181,6 +195,8 @@ SMALL = [
     ("varlen-ragged", synth.VARLEN, dict(seqlens=[37, 0, 130, 64, 1, 300], heads=3), False, 128, 64),
     ("varlen-ragged-causal", synth.VARLEN, dict(seqlens=[37, 0, 130, 64, 1, 300], heads=3), True, 128, 64),
     ("B1N577H2d128-blk256x256-causal", synth.LONG, dict(seqlen=577, batch=1, heads=2), True, 256, 256),
+    ("B2N333H3d128-blk1x64", synth.TEXT, dict(seqlen=333, batch=2, heads=3), False, 1, 64),
+    ("varlen-ragged-causal-blk1x16", synth.VARLEN, dict(seqlens=[37, 0, 130, 64, 1, 300], heads=3), True, 1, 16),
 ]
 
 

@@ -427,3 +427,31 @@ def test_smooth_v_helps_channels_with_an_offset():
     assert c_smooth >= 0.99
     assert c_smooth > c_plain + 0.01
     assert np.abs(o_smooth - ref).max() < 0.5 * np.abs(o_plain - ref).max()
+
+
+# ---------------------------------------------------------------- per-token Q scales (blk_q = 1)
+
+def test_per_token_q_scales():
+    rng = np.random.default_rng(31)
+    L, H, d = 50, 2, 64
+    # every 16th row is an outlier 15x larger: one scale per block leaves the other
+    # rows of its block ~8 levels, one scale per token keeps their 127
+    mag = np.full((1, L, H, 1), 2.0)
+    mag[:, ::16] = 30.0
+    q = (rng.standard_normal((1, L, H, d)) * mag).astype(np.float16)
+    k = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    qd = O.quantize_qk(q, k, [L], None, 1, 16)
+    assert qd["sq"].shape[-1] == L
+    qf = O.fold_sm_scale(q[0, :, 0, :], O.default_sm_scale(d))
+    for n in range(L):
+        # every row's scale is its own absmax / 127 and the absmax element codes to +-127
+        assert qd["sq"][0, 0, n] == np.float32(np.float32(np.abs(qf[n]).max()) / np.float32(127))
+        assert np.abs(qd["q8"][0, n, 0].astype(np.int32)).max() == 127
+    ref = O.exact_attention(q, k, v, [L], None, False)
+    o1, _ = O.sage_attn(q, k, v, [L], None, False, 1, 16)
+    o64, _ = O.sage_attn(q, k, v, [L], None, False, 64, 16)
+    rows = np.arange(L) % 16 != 0                       # the non-outlier rows
+    e1, e64 = np.abs(o1 - ref)[:, rows].max(), np.abs(o64 - ref)[:, rows].max()
+    assert e1 < 0.5 * e64
+    assert cos(o1, ref) > cos(o64, ref)
