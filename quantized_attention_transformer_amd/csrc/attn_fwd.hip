@@ -113,6 +113,11 @@ struct Lds {
   static constexpr int KSTAB = RING > MERGE ? RING : MERGE;  // per-tile k_scale table (key blocks of 64k keys)
   static constexpr int KSCAP = 4096;                          // its capacity in tiles
   static constexpr int BYTES = KSTAB + 4 * KSCAP;
+  // fp16 O rows staged for the stores (after the merge, past the merge area);
+  // rows padded by 16 bytes against bank conflicts on the writes
+  static constexpr int OROW = 2 * D + 16;
+  static constexpr int OSTAGE = MERGE;
+  static_assert(OSTAGE + BM * OROW <= BYTES, "O staging fits the workgroup's LDS");
   static constexpr int KCH = KBYTES / 1024;             // 1 KiB DMA blocks per K tile
   static constexpr int VCH = FP8 ? 0 : VBYTES / 1024;   // (fp16 V)
   __device__ static constexpr int kswz(int r) { return (r / (256 / D)) % (D / 16); }
@@ -343,12 +348,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     vaddr[ct] = vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
   }
 
-  // LDS starts zeroed so bytes the tail tiles leave untouched are finite.
-  for (int x = tid; x < S::RING / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
   const bool ks_in_lds = KSU && ntiles <= S::KSCAP;
-  if (ks_in_lds)
-    for (int t = tid; t < ntiles; t += NT) *(LDS float*)(lds + S::KSTAB + 4 * t) = ksc[(t * BN) / p.blk_k];
-  __syncthreads();
 
   DmaPlan<D, FP8> dma;
   dma.init(w & 3, lane, kn, vn);  // the plan covers a tile with the 4 waves of one half
@@ -601,8 +601,21 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   };
 
-  // ---- prologue: half h loads K(h), K(h+2) and V(h) (empty descriptors past the end)
+  // ---- prologue.  LDS starts zeroed, so bytes the tail tiles leave untouched
+  // are finite; then, in one batch of loads in flight together with the Q
+  // fragments: half h's tiles K(h), K(h+2) and V(h) (empty descriptors past the
+  // end) and the per-tile k_scale table.
+  for (int x = tid; x < S::RING / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
+  __syncthreads();  // the zeroes are in place before any tile lands
   {
+    constexpr int KSPT = S::KSCAP / NT;  // k_scale table entries per thread
+    float ksv[KSPT];
+    if (ks_in_lds)
+#pragma unroll
+      for (int j = 0; j < KSPT; ++j) {
+        const int t = tid + j * NT;
+        ksv[j] = t < ntiles ? ksc[(t * BN) / p.blk_k] : 0.0f;
+      }
     if constexpr (FP8)
       v8s.load(vseq, vn, hf * BN, L, tidh);
     else
@@ -615,6 +628,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     krec -= 2 * kstep;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
+    if (ks_in_lds)
+#pragma unroll
+      for (int j = 0; j < KSPT; ++j) {
+        const int t = tid + j * NT;
+        if (t < ntiles) *(LDS float*)(lds + S::KSTAB + 4 * t) = ksv[j];
+      }
   }
   // The compiler's own bookkeeping of outstanding loads (Q, the k_scale
   // table) ends here: it must not add waits for them inside the loop, where
@@ -802,29 +821,38 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const float wa = mref_own == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref_own - mmax);
   const float wb = mref_b == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref_b - mmax);
 
-  // ---- epilogue: O = O^T / l (FP8: l and O both carry the factor 448; times v_scale)
-  _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h);
+  // ---- epilogue: O = O^T / l (FP8: l and O both carry the factor 448; times
+  // v_scale).  A lane holds 4-channel pieces of its row; the fp16 rows go
+  // through LDS so that the stores write whole rows (16 lanes per row).
   const float inv = 1.0f / xhalf_sum(lsum * wa + lsum_b * wb);
-  if (i < L) {
-    _Float16* orow = obase + (int64_t)i * a.os.n;
+  lds_u8* const ostage = lds + S::OSTAGE;
 #pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
+  for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cc = 32 * ct + 8 * q + 4 * g;
-        float f[4];
+    for (int q = 0; q < 4; ++q) {
+      const int cc = 32 * ct + 8 * q + 4 * g;
+      float f[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q + e;
-          f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
-          if constexpr (FP8) {
-            f[e] *= a.v_scale[sh * D + cc + e];
-            if (a.v_mean) f[e] += a.v_mean[sh * D + cc + e];  // smoothed V: P (V - mean) + mean
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q + e;
+        f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
+        if constexpr (FP8) {
+          f[e] *= a.v_scale[sh * D + cc + e];
+          if (a.v_mean) f[e] += a.v_mean[sh * D + cc + e];  // smoothed V: P (V - mean) + mean
         }
-        const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
-        *reinterpret_cast<v4h*>(orow + cc) = hv;
       }
+      const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
+      *(LDS v4h*)(ostage + (i - q0) * S::OROW + 2 * cc) = hv;
+    }
+  __syncthreads();  // (half 1 has ended: the barrier waits for half 0's waves)
+  _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h);
+  constexpr int CPR = D / 8;  // 16-byte pieces per row
+#pragma unroll
+  for (int x = 0; x < BM * CPR / (NT / 2); ++x) {
+    const int c = tid + x * (NT / 2), rr = c / CPR, cp = c % CPR;
+    if (q0 + rr < L)
+      *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) =
+          *(const LDS v4i*)(ostage + rr * S::OROW + 16 * cp);
   }
 }
 
