@@ -52,6 +52,10 @@ Steps, in the pages' order:
     448 / l with l from the unquantised p.  E4M3 is the OCP format (bias 7, max 448, no
     infinities), round-to-nearest-even, saturating at 448.
 
+K and V may have fewer heads than Q (grouped-query attention, which the
+scaled-dot-product-attention interface the pages' drop-in replaces accepts):
+query head h reads K/V head h // (Hq / Hk), and K's mean is per K head.
+
 Readings of points the pages leave open are listed with the design notes
 (mean over tokens per channel; fp32 smoothed K fed to the quantiser; IEEE
 division rather than a reciprocal multiply; symmetric [-127, 127]; scale 0 for
@@ -140,24 +144,27 @@ def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Option
     """Steps 1-4 for every (sequence, head).
 
     q, k: fp16 in [B, N, H, d] (dense, cu None) or [T, H, d] (packed, cu int32
-    prefix offsets).  Returns a dict with q8, k8 (int8, same layout as the
-    input), sq [nseq, H, ceil(maxL/blk_q)], sk [nseq, H, ceil(maxL/blk_k)]
-    (entries past a sequence's last block are 0) and km [nseq, H, d] fp32.
-    smooth=False is the ablation without mean subtraction (km is then 0)."""
+    prefix offsets); k may have fewer heads Hk than q (grouped-query
+    attention: Hq a multiple of Hk).  Returns a dict with q8, k8 (int8, same
+    layout as the input), sq [nseq, Hq, ceil(maxL/blk_q)], sk [nseq, Hk,
+    ceil(maxL/blk_k)] (entries past a sequence's last block are 0) and km
+    [nseq, Hk, d] fp32 (the mean is per K head).  smooth=False is the ablation
+    without mean subtraction (km is then 0)."""
     nseq = len(seqlens)
     H, d = q.shape[-2], q.shape[-1]
+    Hk = k.shape[-2]
     maxL = int(max(seqlens)) if nseq else 0
     sm = default_sm_scale(d) if sm_scale is None else np.float32(sm_scale)
     q8 = np.zeros(q.shape, np.int8)
     k8 = np.zeros(k.shape, np.int8)
     sq = np.zeros((nseq, H, -(-maxL // blk_q)), np.float32)
-    sk = np.zeros((nseq, H, -(-maxL // blk_k)), np.float32)
-    km = np.zeros((nseq, H, d), np.float32)
+    sk = np.zeros((nseq, Hk, -(-maxL // blk_k)), np.float32)
+    km = np.zeros((nseq, Hk, d), np.float32)
     qv, kv = _seq_views(q, cu, nseq), _seq_views(k, cu, nseq)
     q8v, k8v = _seq_views(q8, cu, nseq), _seq_views(k8, cu, nseq)
     for s in range(nseq):
         L = int(seqlens[s])
-        for h in range(H):
+        for h in range(Hk):
             kh = kv[s][:L, h, :]
             if smooth:
                 km[s, h] = k_mean(kh)
@@ -167,6 +174,7 @@ def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Option
             c, sc = quant_rows(ks, blk_k)
             k8v[s][:L, h, :] = c
             sk[s, h, :len(sc)] = sc
+        for h in range(H):
             c, sc = quant_rows(fold_sm_scale(qv[s][:L, h, :], sm), blk_q)
             q8v[s][:L, h, :] = c
             sq[s, h, :len(sc)] = sc
@@ -328,6 +336,7 @@ def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=
     quantisation dict)."""
     nseq = len(seqlens)
     H = q.shape[-2]
+    grp = H // k.shape[-2]  # query heads per K/V head (grouped-query attention)
     qd = quant if quant is not None else quantize_qk(q, k, seqlens, cu, blk_q, blk_k, sm_scale,
                                                      smooth=smooth)
     if pv_fp8:
@@ -343,11 +352,12 @@ def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=
         if rows_by_seq is not None and rows is None:
             continue
         for h in range(H):
-            o = attention_head(q8v[s][:L, h], k8v[s][:L, h], qd["sq"][s, h], qd["sk"][s, h],
-                               vv[s][:L, h], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8,
-                               v8h=None if v8v is None else v8v[s][:L, h],
-                               svh=None if v8v is None else qd["sv"][s, h],
-                               vmh=qd["vm"][s, h] if (pv_fp8 and smooth_v) else None)
+            kh = h // grp
+            o = attention_head(q8v[s][:L, h], k8v[s][:L, kh], qd["sq"][s, h], qd["sk"][s, kh],
+                               vv[s][:L, kh], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8,
+                               v8h=None if v8v is None else v8v[s][:L, kh],
+                               svh=None if v8v is None else qd["sv"][s, kh],
+                               vmh=qd["vm"][s, kh] if (pv_fp8 and smooth_v) else None)
             if rows is None:
                 ov[s][:L, h] = o
             else:
@@ -360,6 +370,7 @@ def exact_attention(q, k, v, seqlens, cu, causal, sm_scale=None, rows_by_seq=Non
     (the result the quantised method approximates; [SA2] "即插即用举例")."""
     nseq = len(seqlens)
     H, d = q.shape[-2], q.shape[-1]
+    grp = H // k.shape[-2]
     sm = float(default_sm_scale(d) if sm_scale is None else np.float32(sm_scale))
     O = np.full(q.shape, np.nan, np.float64)
     ov = _seq_views(O, cu, nseq)
@@ -371,9 +382,9 @@ def exact_attention(q, k, v, seqlens, cu, causal, sm_scale=None, rows_by_seq=Non
             continue
         rows = np.asarray(rows)
         for h in range(H):
-            S = (qv[s][rows, h].astype(np.float64) @ kv[s][:L, h].astype(np.float64).T) * sm
+            S = (qv[s][rows, h].astype(np.float64) @ kv[s][:L, h // grp].astype(np.float64).T) * sm
             if causal:
                 S = np.where(np.arange(L)[None, :] <= rows[:, None], S, -np.inf)
             P = np.exp(S - S.max(axis=1, keepdims=True))
-            ov[s][rows, h] = (P @ vv[s][:L, h].astype(np.float64)) / P.sum(axis=1, keepdims=True)
+            ov[s][rows, h] = (P @ vv[s][:L, h // grp].astype(np.float64)) / P.sum(axis=1, keepdims=True)
     return O

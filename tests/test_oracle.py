@@ -455,3 +455,24 @@ def test_per_token_q_scales():
     e1, e64 = np.abs(o1 - ref)[:, rows].max(), np.abs(o64 - ref)[:, rows].max()
     assert e1 < 0.5 * e64
     assert cos(o1, ref) > cos(o64, ref)
+
+
+# ---------------------------------------------------------------- grouped-query attention
+
+@pytest.mark.parametrize("hk", [1, 2])
+def test_gqa_equals_repeated_kv_heads(hk):
+    rng = np.random.default_rng(41)
+    L, H, d = 70, 4, 64
+    q = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    k = (rng.standard_normal((1, L, hk, d)) + 3 * rng.standard_normal((1, 1, hk, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, hk, d)).astype(np.float16)
+    rep = lambda x: np.repeat(x, H // hk, axis=2)  # noqa: E731  query head h reads K/V head h // (H / hk)
+    for causal in (False, True):
+        for fp8 in (False, True):
+            og, qg = O.sage_attn(q, k, v, [L], None, causal, 32, 16, pv_fp8=fp8)
+            om, qm = O.sage_attn(q, rep(k), rep(v), [L], None, causal, 32, 16, pv_fp8=fp8)
+            np.testing.assert_array_equal(og, om)
+            np.testing.assert_array_equal(qg["km"], qm["km"][:, ::H // hk])
+            np.testing.assert_array_equal(qg["k8"], qm["k8"][:, :, ::H // hk])
+        np.testing.assert_array_equal(O.exact_attention(q, k, v, [L], None, causal),
+                                      O.exact_attention(q, rep(k), rep(v), [L], None, causal))
