@@ -32,10 +32,13 @@
  *   (S.s is ignored).  The channel stride is 1.  Base pointers must be
  *   16-byte aligned and S.h, S.n multiples of 8 elements (fp16) / 16 (8-bit).
  *   Q, K, V, O are fp16.  q8/k8 are int8; v8 is OCP FP8 E4M3 (uint8).
+ * Heads.  Q and O have `heads` heads; K, V, k8, v8 have kv_heads (0: the
+ *   same).  A problem that describes V alone (sage_quantize_v_fp8*) uses
+ *   `heads` for V's heads.
  * Scales.  q_scale [nseq][heads][ceil(max_seqlen/blk_q)] and k_scale
- *   [nseq][heads][ceil(max_seqlen/blk_k)] fp32, contiguous; entries past a
+ *   [nseq][kv_heads][ceil(max_seqlen/blk_k)] fp32, contiguous; entries past a
  *   sequence's last block are left unspecified.  k_mean and v_scale are
- *   [nseq][heads][head_dim] fp32, contiguous.
+ *   [nseq][kv_heads][head_dim] fp32, contiguous.
  * Blocks.  blk_q and blk_k: quantisation block lengths in tokens, multiples
  *   of 16 in [16, 256]; blk_q may also be 1, one Q scale per token (finer
  *   than per-block, as [SA2] 技术方案 item 2 argues; in the fused kernel each
@@ -90,6 +93,9 @@ typedef struct {
   const int32_t* cu_seqlens;  /* device pointer, nseq+1 entries; NULL = dense      */
   int32_t blk_q;              /* Q quantisation block (tokens)                     */
   int32_t blk_k;              /* K quantisation block (tokens)                     */
+  int32_t kv_heads;           /* heads of K and V; 0 = heads.  Fewer (a divisor of
+                                 heads): grouped-query attention, query head h
+                                 reads K/V head h / (heads / kv_heads)            */
 } sage_problem;
 
 /* Bytes of workspace sage_attn and sage_quantize need for this problem

@@ -288,14 +288,21 @@ template <int D, bool FP8, bool CAUSAL, bool KSU>
 __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, lds_u8* const lds) {
   using S = Lds<D, FP8>;
 
-  // ---- workgroup -> (sequence, head, query tile): pair = 8 * slot + xcd
+  // ---- workgroup -> (sequence, head, query tile).  (sequence, K/V head)
+  // groups are dealt round-robin over the 8 XCDs, group = 8 * (slot / grp) +
+  // xcd, and an XCD runs the grp query heads of a group (grouped-query
+  // attention; grp = 1 otherwise) and all their query tiles back to back, so
+  // a K/V head is read into one L2.
   const int nqt = (p.max_seqlen + BM - 1) / BM;
+  const int grp = p.heads / p.kv_heads;
   const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
-  const int sh_i = (kx / nqt) * 8 + xcd;
-  if (sh_i >= p.nseq * p.heads) return;
+  const int slot = kx / nqt;
+  const int kvg = (slot / grp) * 8 + xcd;
+  if (kvg >= p.nseq * p.kv_heads) return;
   const int qt = CAUSAL ? nqt - 1 - kx % nqt : kx % nqt;
-  const int s = sh_i / p.heads, h = sh_i % p.heads;
-  const int64_t sh = sh_i;
+  const int s = kvg / p.kv_heads, kvh = kvg % p.kv_heads, h = kvh * grp + slot % grp;
+  const int64_t sh = (int64_t)s * p.heads + h;  // (sequence, query head)
+  const int64_t skv = kvg;                       // (sequence, K/V head)
 
   const int L = seq_len(p.cu, s, p.max_seqlen);
   const int q0 = qt * BM;
@@ -305,10 +312,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int hf = w >> 2;  // half: key tiles t = hf (mod 2)
 
   const int8_t* __restrict__ qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h);
-  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, h);
-  const uint8_t* vseq = (const uint8_t*)a.v + seq_head_base(p.cu, a.vs, s, h) * (FP8 ? 1 : 2);
+  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, kvh);
+  const uint8_t* vseq = (const uint8_t*)a.v + seq_head_base(p.cu, a.vs, s, kvh) * (FP8 ? 1 : 2);
   const int64_t kn = a.k8s.n, vn = a.vs.n * (FP8 ? 1 : 2);  // row strides in bytes
-  const float* __restrict__ ksc = a.k_scale + sh * p.nbk;
+  const float* __restrict__ ksc = a.k_scale + skv * p.nbk;
   const __attribute__((address_space(4))) float* ksc_c = (const __attribute__((address_space(4))) float*)ksc;
 
   // ---- this lane's query row and its Q fragments (B operand of S^T)
@@ -837,8 +844,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         const int r = 4 * q + e;
         f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
         if constexpr (FP8) {
-          f[e] *= a.v_scale[sh * D + cc + e];
-          if (a.v_mean) f[e] += a.v_mean[sh * D + cc + e];  // smoothed V: P (V - mean) + mean
+          f[e] *= a.v_scale[skv * D + cc + e];
+          if (a.v_mean) f[e] += a.v_mean[skv * D + cc + e];  // smoothed V: P (V - mean) + mean
         }
       }
       const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
@@ -878,7 +885,7 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t sh = (int64_t)s * H + h;
   const int8_t* qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h);
-  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, h);
+  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, h / (p.heads / p.kv_heads));
   const int i = q0 + w * 32 + li;
   v4i qf[D / 32];
 #pragma unroll
@@ -920,7 +927,8 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
 template <int D, bool FP8, bool CAUSAL, bool KSU>
 hipError_t launch_cfg(const Problem& p, const AttnArgs& a, hipStream_t st) {
   const int nqt = (p.max_seqlen + BM - 1) / BM;
-  const int64_t P8 = ((int64_t)p.nseq * p.heads + 7) / 8 * 8;
+  // slots per XCD: ceil(groups / 8) groups of heads/kv_heads query heads
+  const int64_t P8 = ((int64_t)p.nseq * p.kv_heads + 7) / 8 * 8 * (p.heads / p.kv_heads);
   const int64_t G = (int64_t)nqt * P8;
   if (G >= (1ll << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU>), dim3((unsigned)G), dim3(NT), 0, st, p, a);

@@ -202,15 +202,17 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
   return scale;
 }
 
-// grid (nqw + nks, heads, nseq), kQThreads.  Workgroups x < nqw quantise Q
+// grid (nqw + nks, heads, nseq), kQThreads (heads: of Q).  Workgroups x < nqw quantise Q
 // (INT8 Q' = Q * sm_scale): block x of blk_q rows, or for blk_q == 1 (one
 // scale per token) the RPP rows x*RPP .. x*RPP+RPP-1, TPR threads per row.
-// Workgroups x >= nqw take the fp64 column sums of K over the tokens of chunk
-// x - nqw (kKSumRows tokens), one partial per chunk.
+// Workgroups x >= nqw with a K head (y < kv_heads) take the fp64 column sums
+// of K over the tokens of chunk x - nqw (kKSumRows tokens), one partial per
+// chunk.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
-    int max_seqlen, int blk_q, int nbq, int nqw, int nks, float sm_scale, int8_t* __restrict__ q8, Str q8s,
+    int max_seqlen, int blk_q, int nbq, int nqw, int nks, int kv_heads, float sm_scale, int8_t* __restrict__ q8,
+    Str q8s,
     float* __restrict__ sq, double* __restrict__ part) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
@@ -250,7 +252,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     if (tid == 0) sq[sh * nbq + x] = scale;
     return;
   }
-  // K column sums (exact in fp64, in any order)
+  // K column sums (exact in fp64, in any order), over the K heads only
+  if (h >= kv_heads) return;
+  const int64_t skv = (int64_t)s * kv_heads + h;
   const int ci = x - nqw;
   const int n0 = ci * kKSumRows;
   if (n0 >= L) return;
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     double t = 0.0;
 #pragma unroll
     for (int i = 0; i < RPP; ++i) t += red[i][tid];
-    part[(sh * nks + ci) * D + tid] = t;
+    part[(skv * nks + ci) * D + tid] = t;
   }
 }
 
@@ -304,7 +308,7 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
   return sum;
 }
 
-// grid (heads, nseq), kQThreads: mean = fp32(sum / L) from the per-Q-block
+// grid (kv heads, nseq), kQThreads: mean = fp32(sum / L) from the
 // partials (long sequences; shorter ones fold this into k_quant_k).
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __res
   if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(sum / (double)L) : 0.0f;
 }
 
-// grid (nbk, heads, nseq), kQThreads: K block bi -> INT8 K' = K - mean(K).
+// grid (nbk, kv heads, nseq), kQThreads: K block bi -> INT8 K' = K - mean(K).
 // FOLD: the workgroup sums the column partials itself (every block of the
 // head does; block 0 stores k_mean), with the block's K rows already in
 // flight; otherwise k_mean comes from k_mean_finalize.
@@ -407,7 +411,7 @@ __global__ void k_v_scale(float* __restrict__ sv, int64_t n) {
   if (i < n) sv[i] = sv[i] / 448.0f;
 }
 
-// grid (nchunk, heads, nseq): E4M3 codes of V (vmean != nullptr: of V' =
+// grid (nchunk, kv heads, nseq): E4M3 codes of V (vmean != nullptr: of V' =
 // fp32(V - vmean), the smoothed V) with the per-channel scales sv.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict__ V, Str vs,
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
 // of V'.  x -> fp32(x - mean) is monotone, so max|V'| of a channel comes from
 // its fp16 maximum and minimum.
 
-// grid (nchunk, heads, nseq), kThreads: per chunk of kColChunk tokens and
+// grid (nchunk, kv heads, nseq), kThreads: per chunk of kColChunk tokens and
 // channel, the exact fp64 sum and the fp16 maximum and minimum (as float).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restrict__ V, Str vs,
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restr
   }
 }
 
-// grid (heads, nseq), D threads: mean = fp32(sum / L); scale = fp32(max(|fp32(max -
+// grid (kv heads, nseq), D threads: mean = fp32(sum / L); scale = fp32(max(|fp32(max -
 // mean)|, |fp32(min - mean)|) / 448) per channel (0 for an empty sequence).
 template <int D>
 __global__ __launch_bounds__(D) void k_v_finalize(const double* __restrict__ psum, const float* __restrict__ pmax,
@@ -556,21 +560,21 @@ hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const 
     const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
     hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st,
                        (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.nbq, nqw,
-                       p.nks, sm_scale, q8, q8s, q_scale, partial);
+                       p.nks, p.kv_heads, sm_scale, q8, q8s, q_scale, partial);
   });
   return hipGetLastError();
 }
 
 hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
                           Str k8s, float* k_scale, hipStream_t st) {
-  dim3 grid(p.nbk, p.heads, p.nseq);
+  dim3 grid(p.nbk, p.kv_heads, p.nseq);
   if (p.nks <= kFoldMaxBlocks) {
     SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
                                                    (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
                                                    partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st,
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
                                                  partial, p.cu, p.max_seqlen, p.nks, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -581,23 +585,23 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
 }
 
 hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* vmax, hipStream_t st) {
-  const int64_t n = (int64_t)p.nseq * p.heads * p.head_dim;
+  const int64_t n = (int64_t)p.nseq * p.kv_heads * p.head_dim;
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vmax, n);
-  dim3 grid(p.nchunk, p.heads, p.nseq);
+  dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colmax<D>), grid, dim3(kThreads), 0, st,
                                                  (const _Float16*)V, vs, p.cu, p.max_seqlen, vmax));
   return hipGetLastError();
 }
 
 hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st) {
-  const int64_t n = (int64_t)p.nseq * p.heads * p.head_dim;
+  const int64_t n = (int64_t)p.nseq * p.kv_heads * p.head_dim;
   hipLaunchKernelGGL(k_v_scale, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, v_scale, n);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* v_scale, const float* v_mean,
                           uint8_t* v8, Str v8s, hipStream_t st) {
-  dim3 grid(p.nchunk, p.heads, p.nseq);
+  dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_v<D>), grid, dim3(kThreads), 0, st,
                                                  (const _Float16*)V, vs, p.cu, p.max_seqlen, v_scale, v_mean, v8,
                                                  v8s));
@@ -606,13 +610,13 @@ hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* 
 
 hipError_t launch_v_smooth_stats(const Problem& p, const void* V, Str vs, double* psum, float* pmax, float* pmin,
                                  float* v_scale, float* v_mean, hipStream_t st) {
-  dim3 grid(p.nchunk, p.heads, p.nseq);
+  dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colstats<D>), grid, dim3(kThreads), 0, st,
                                                  (const _Float16*)V, vs, p.cu, p.max_seqlen, p.nchunk, psum, pmax,
                                                  pmin));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_finalize<D>), dim3(p.heads, p.nseq), dim3(D), 0, st, psum,
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(D), 0, st, psum,
                                                  pmax, pmin, p.cu, p.max_seqlen, p.nchunk, v_scale, v_mean));
   return hipGetLastError();
 }

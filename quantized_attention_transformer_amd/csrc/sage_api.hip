@@ -49,6 +49,9 @@ int check_problem(const sage_problem* p) {
                 p->blk_q, p->blk_k);
   if (p->cu_seqlens && p->total_tokens < 0) return fail(SAGE_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (p->heads > 65535 || p->nseq > 65535) return fail(SAGE_ERR_UNSUPPORTED, "heads and nseq must be <= 65535");
+  if (p->kv_heads < 0 || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
+    return fail(SAGE_ERR_INVALID_ARG, "kv_heads (%d) must divide heads (%d) (0: same as heads)", p->kv_heads,
+                p->heads);
   return SAGE_OK;
 }
 
@@ -59,6 +62,7 @@ sage::Problem to_internal(const sage_problem* p) {
   q.cu = p->cu_seqlens;
   q.nseq = p->nseq;
   q.heads = p->heads;
+  q.kv_heads = p->kv_heads > 0 ? p->kv_heads : p->heads;
   q.max_seqlen = p->max_seqlen;
   q.head_dim = p->head_dim;
   q.blk_q = p->blk_q;
@@ -95,12 +99,14 @@ int64_t tokens(const sage_problem* p) {
   return p->cu_seqlens ? p->total_tokens : (int64_t)p->nseq * p->max_seqlen;
 }
 
+int kv_heads_of(const sage_problem* p) { return p->kv_heads > 0 ? p->kv_heads : p->heads; }
+
 // Workspace layout of sage_attn (offsets in bytes).  int8 Q/K (and E4M3 V)
 // are stored head-major: dense [nseq][heads][max_seqlen][d], packed
-// [heads][total_tokens][d].
+// [heads][total_tokens][d] (K and V with kv_heads heads).
 struct WsLayout {
   size_t q8, k8, sq, sk, km, colsum, v8, sv, vpsum, vpmax, vpmin, total;
-  sage_strides s8;
+  sage_strides s8q, s8kv;
 };
 
 bool valid_pv_mode(int m) { return m == SAGE_PV_FP16 || m == SAGE_PV_FP8 || m == SAGE_PV_FP8_SMOOTH_V; }
@@ -112,7 +118,7 @@ struct VSmoothWs {
 
 VSmoothWs v_smooth_ws(const sage_problem* p, size_t base) {
   const sage::Problem q = to_internal(p);
-  const size_t n = (size_t)p->nseq * p->heads * q.nchunk * p->head_dim;
+  const size_t n = (size_t)p->nseq * q.kv_heads * q.nchunk * p->head_dim;
   VSmoothWs w{};
   w.psum = base;
   w.pmax = w.psum + align_up(n * 8);
@@ -124,7 +130,7 @@ VSmoothWs v_smooth_ws(const sage_problem* p, size_t base) {
 WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   const sage::Problem q = to_internal(p);
   const int64_t T = tokens(p);
-  const int64_t d = p->head_dim, H = p->heads;
+  const int64_t d = p->head_dim, H = p->heads, Hk = q.kv_heads;
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -133,15 +139,15 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
     return o;
   };
   w.q8 = take((size_t)(T * H * d));
-  w.k8 = take((size_t)(T * H * d));
+  w.k8 = take((size_t)(T * Hk * d));
   w.sq = take((size_t)p->nseq * H * q.nbq * 4);
-  w.sk = take((size_t)p->nseq * H * q.nbk * 4);
-  w.km = take((size_t)p->nseq * H * d * 4);
-  w.colsum = take((size_t)p->nseq * H * q.nks * d * 8);
+  w.sk = take((size_t)p->nseq * Hk * q.nbk * 4);
+  w.km = take((size_t)p->nseq * Hk * d * 4);
+  w.colsum = take((size_t)p->nseq * Hk * q.nks * d * 8);
   if (pv_mode == SAGE_PV_FP8 || pv_mode == SAGE_PV_FP8_SMOOTH_V) {
-    w.v8 = take((size_t)(T * H * d));
+    w.v8 = take((size_t)(T * Hk * d));
     // scales (then, smoothed V: the means)
-    w.sv = take((size_t)p->nseq * H * d * 4 * (pv_mode == SAGE_PV_FP8_SMOOTH_V ? 2 : 1));
+    w.sv = take((size_t)p->nseq * Hk * d * 4 * (pv_mode == SAGE_PV_FP8_SMOOTH_V ? 2 : 1));
   }
   if (pv_mode == SAGE_PV_FP8_SMOOTH_V) {
     const VSmoothWs v = v_smooth_ws(p, off);
@@ -151,16 +157,19 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
     off += v.total;
   }
   w.total = off;
-  if (p->cu_seqlens)
-    w.s8 = sage_strides{0, T * d, d};
-  else
-    w.s8 = sage_strides{H * p->max_seqlen * d, p->max_seqlen * d, d};
+  if (p->cu_seqlens) {
+    w.s8q = sage_strides{0, T * d, d};
+    w.s8kv = w.s8q;
+  } else {
+    w.s8q = sage_strides{H * p->max_seqlen * d, p->max_seqlen * d, d};
+    w.s8kv = sage_strides{Hk * p->max_seqlen * d, p->max_seqlen * d, d};
+  }
   return w;
 }
 
 size_t quantize_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
-  return align_up((size_t)p->nseq * p->heads * q.nks * p->head_dim * 8);
+  return align_up((size_t)p->nseq * q.kv_heads * q.nks * p->head_dim * 8);
 }
 
 int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
@@ -192,7 +201,7 @@ int run_quantize_v(const sage_problem* p, const void* V, sage_strides vs, uint8_
 int run_quantize_v_smooth(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
                           float* v_scale_mean, char* ws, const VSmoothWs& w, hipStream_t st) {
   const sage::Problem q = to_internal(p);
-  float* const vmean = v_scale_mean + (size_t)p->nseq * p->heads * p->head_dim;
+  float* const vmean = v_scale_mean + (size_t)p->nseq * kv_heads_of(p) * p->head_dim;
   hipError_t e;
   if ((e = sage::launch_v_smooth_stats(q, V, S(vs), (double*)(ws + w.psum), (float*)(ws + w.pmax),
                                        (float*)(ws + w.pmin), v_scale_mean, vmean, st)) != hipSuccess)
@@ -288,7 +297,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
   if (!q_scale || !k_scale || (fp8 && !v_scale)) return fail(SAGE_ERR_INVALID_ARG, "scales must not be NULL");
   if ((rc = check_row_span("k8", k8s, 1, p)) || (rc = check_row_span("V", vs, fp8 ? 1 : 2, p))) return rc;
   const float* v_mean =
-      pv_mode == SAGE_PV_FP8_SMOOTH_V ? v_scale + (size_t)p->nseq * p->heads * p->head_dim : nullptr;
+      pv_mode == SAGE_PV_FP8_SMOOTH_V ? v_scale + (size_t)p->nseq * kv_heads_of(p) * p->head_dim : nullptr;
   sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr, v_mean};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -316,7 +325,7 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   int8_t* k8 = (int8_t*)(ws + w.k8);
   float* sq = (float*)(ws + w.sq);
   float* sk = (float*)(ws + w.sk);
-  if ((rc = run_quantize(p, Q, qs, K, ks, sm_scale, q8, w.s8, k8, w.s8, sq, sk, (float*)(ws + w.km),
+  if ((rc = run_quantize(p, Q, qs, K, ks, sm_scale, q8, w.s8q, k8, w.s8kv, sq, sk, (float*)(ws + w.km),
                          (double*)(ws + w.colsum), st)))
     return rc;
   const void* vin = V;
@@ -324,20 +333,20 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   const float* sv = nullptr;
   const float* vmean = nullptr;
   if (pv_mode == SAGE_PV_FP8) {
-    if ((rc = run_quantize_v(p, V, vs, (uint8_t*)(ws + w.v8), w.s8, (float*)(ws + w.sv), st)))
+    if ((rc = run_quantize_v(p, V, vs, (uint8_t*)(ws + w.v8), w.s8kv, (float*)(ws + w.sv), st)))
       return rc;
   } else if (pv_mode == SAGE_PV_FP8_SMOOTH_V) {
     const VSmoothWs vw{w.vpsum, w.vpmax, w.vpmin, 0};
-    if ((rc = run_quantize_v_smooth(p, V, vs, (uint8_t*)(ws + w.v8), w.s8, (float*)(ws + w.sv), ws, vw, st)))
+    if ((rc = run_quantize_v_smooth(p, V, vs, (uint8_t*)(ws + w.v8), w.s8kv, (float*)(ws + w.sv), ws, vw, st)))
       return rc;
-    vmean = (const float*)(ws + w.sv) + (size_t)p->nseq * p->heads * p->head_dim;
+    vmean = (const float*)(ws + w.sv) + (size_t)p->nseq * kv_heads_of(p) * p->head_dim;
   }
   if (pv_mode != SAGE_PV_FP16) {
     vin = ws + w.v8;
-    vin_s = w.s8;
+    vin_s = w.s8kv;
     sv = (const float*)(ws + w.sv);
   }
-  sage::AttnArgs a{q8, S(w.s8), k8, S(w.s8), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean};
+  sage::AttnArgs a{q8, S(w.s8q), k8, S(w.s8kv), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode != SAGE_PV_FP16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;

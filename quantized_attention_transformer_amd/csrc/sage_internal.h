@@ -30,13 +30,14 @@ __device__ __forceinline__ int64_t seq_head_base(const int32_t* cu, Str st, int 
 struct Problem {
   const int32_t* cu;
   int nseq, heads, max_seqlen, head_dim, blk_q, blk_k;
+  int kv_heads;          // heads of K and V (grouped-query attention: heads % kv_heads == 0)
   int nbq, nbk, nchunk;  // ceil(max_seqlen/blk_q), ceil(max_seqlen/blk_k), ceil(max_seqlen/kColChunk)
   int nks;               // ceil(max_seqlen/kKSumRows): K column-sum partials per (sequence, head)
 };
 
 // ---- pre-pass (prepass.hip) ----
 // INT8 Q blocks (blk_q == 1: one scale per token), plus fp64 column sums of K over chunks of
-// kKSumRows tokens (partial: nseq*heads*nks*head_dim).
+// kKSumRows tokens (partial: nseq*kv_heads*nks*head_dim).
 hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st);
 // k_mean = fp32(sum of the partials / L) per (sequence, head, channel), and INT8 K blocks of K - k_mean.

@@ -37,7 +37,7 @@ class Strides(ctypes.Structure):
 class Problem(ctypes.Structure):
     _fields_ = [("nseq", ctypes.c_int32), ("heads", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("total_tokens", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
-                ("blk_q", ctypes.c_int32), ("blk_k", ctypes.c_int32)]
+                ("blk_q", ctypes.c_int32), ("blk_k", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
 
 
 class SageError(RuntimeError):
@@ -98,8 +98,25 @@ def strides_of(t: torch.Tensor, layout: str) -> Strides:
     raise ValueError(f"unknown layout {layout!r}")
 
 
+def heads_of(t: torch.Tensor, layout: str = "bnhd", packed: bool = False) -> int:
+    """Number of heads of a [B, N, H, d] ("bnhd"), [B, H, N, d] ("bhnd") or packed [T, H, d] tensor."""
+    if packed:
+        return t.shape[1]
+    return t.shape[2] if layout == "bnhd" else t.shape[1]
+
+
 def make_problem(q: torch.Tensor, layout: str = "bnhd", cu_seqlens: Optional[torch.Tensor] = None,
-                 max_seqlen: Optional[int] = None, blk_q: int = 128, blk_k: int = 64) -> Problem:
+                 max_seqlen: Optional[int] = None, blk_q: int = 128, blk_k: int = 64,
+                 k: Optional[torch.Tensor] = None) -> Problem:
+    """The sage_problem of q (and, for grouped-query attention, kv_heads from k's head count)."""
+    prob = _make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    if k is not None:
+        hk = heads_of(k, layout, cu_seqlens is not None)
+        prob.kv_heads = 0 if hk == prob.heads else hk
+    return prob
+
+
+def _make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k) -> Problem:
     if cu_seqlens is not None:
         if q.dim() != 3:
             raise ValueError("packed inputs are [T, H, d]")
@@ -134,14 +151,16 @@ def _nblocks(n, b):
 
 def quantize(q, k, *, sm_scale: Optional[float] = None, layout="bnhd", cu_seqlens=None, max_seqlen=None,
              blk_q=128, blk_k=64, workspace=None):
-    """sage_quantize: returns dict(q8, k8 (int8, q's shape and layout), q_scale, k_scale, k_mean)."""
-    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    """sage_quantize: returns dict(q8, k8 (int8, the shapes and layout of q and k), q_scale,
+    k_scale, k_mean).  k may have fewer heads than q (grouped-query attention)."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k, k=k)
     q8 = torch.empty(q.shape, dtype=torch.int8, device=q.device)
     k8 = torch.empty(k.shape, dtype=torch.int8, device=q.device)
     nseq, H, N, d = prob.nseq, prob.heads, prob.max_seqlen, prob.head_dim
+    Hk = prob.kv_heads or H
     sq = torch.zeros((nseq, H, _nblocks(N, blk_q)), dtype=torch.float32, device=q.device)
-    sk = torch.zeros((nseq, H, _nblocks(N, blk_k)), dtype=torch.float32, device=q.device)
-    km = torch.zeros((nseq, H, d), dtype=torch.float32, device=q.device)
+    sk = torch.zeros((nseq, Hk, _nblocks(N, blk_k)), dtype=torch.float32, device=q.device)
+    km = torch.zeros((nseq, Hk, d), dtype=torch.float32, device=q.device)
     nws = quantize_workspace_bytes(prob)
     if workspace is None:
         workspace = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
@@ -178,8 +197,9 @@ def quantize_v_fp8(v, *, layout="bnhd", cu_seqlens=None, max_seqlen=None, smooth
 
 def attn_quantized(q8, k8, q_scale, k_scale, v, *, v_scale=None, causal=False, pv_mode=SAGE_PV_FP16,
                    layout="bnhd", cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None):
-    """sage_attn_quantized: fused attention over quantised inputs; returns O (fp16, q8's shape)."""
-    prob = make_problem(q8, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    """sage_attn_quantized: fused attention over quantised inputs; returns O (fp16, q8's shape).
+    k8 and v may have fewer heads than q8 (grouped-query attention)."""
+    prob = make_problem(q8, layout, cu_seqlens, max_seqlen, blk_q, blk_k, k=k8)
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.float16, device=q8.device)
     rc = lib().sage_attn_quantized(ctypes.byref(prob), _ptr(q8), strides_of(q8, layout), _ptr(k8),
@@ -192,8 +212,9 @@ def attn_quantized(q8, k8, q_scale, k_scale, v, *, v_scale=None, causal=False, p
 
 def attn(q, k, v, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAGE_PV_FP16, layout="bnhd",
          cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None, workspace=None):
-    """sage_attn: the whole forward pass; returns O (fp16, q's shape)."""
-    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k)
+    """sage_attn: the whole forward pass; returns O (fp16, q's shape).  k and v may have
+    fewer heads than q (grouped-query attention)."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k, k=k)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
     nws = workspace_bytes(prob, pv_mode)
@@ -241,3 +262,33 @@ def debug_fp8_mfma(a8: torch.Tensor, b8: torch.Tensor, c: torch.Tensor, scale_a:
     _check("sage_debug_fp8_mfma", lib().sage_debug_fp8_mfma(_ptr(a8), _ptr(b8), _ptr(c), int(scale_a), int(scale_b),
                                                            _ptr(d), _stream()))
     return d
+
+
+def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+                                 enable_gqa=False, *, pv_mode=SAGE_PV_FP16, blk_q=128, blk_k=64):
+    """Drop-in for torch.nn.functional.scaled_dot_product_attention on [B, H, N, d]
+    fp16 tensors (the interface the SageAttention pages replace in one line):
+    softmax(Q K^T * scale) V through sage_attn, with scale = 1/sqrt(d) when None
+    and is_causal masking.  key and value may have fewer heads than query when
+    enable_gqa is set (query head h reads K/V head h / (H / H_kv)), as in
+    torch's function.  No attn_mask and no dropout (they raise).  Returns O in
+    query's shape."""
+    if attn_mask is not None:
+        raise NotImplementedError("attn_mask is not supported (is_causal is)")
+    if dropout_p:
+        raise NotImplementedError("dropout is not supported (inference forward pass)")
+    if query.dim() != 4 or key.dim() != 4 or value.dim() != 4:
+        raise ValueError("query, key and value are [B, H, N, d]")
+    hq, hk = query.shape[1], key.shape[1]
+    if value.shape[1] != hk:
+        raise ValueError("key and value must have the same number of heads")
+    if hk != hq and not enable_gqa:
+        raise ValueError("key/value with fewer heads than query need enable_gqa=True")
+    if hq % hk:
+        raise ValueError(f"query heads ({hq}) must be a multiple of key/value heads ({hk})")
+    if key.shape[2] != query.shape[2]:
+        raise NotImplementedError("self-attention only: query and key have the same length")
+    to16 = lambda t: t if (t.dtype == torch.float16 and t.stride(-1) == 1) else t.to(torch.float16).contiguous()  # noqa: E731
+    q, k, v = to16(query), to16(key), to16(value)
+    return attn(q, k, v, causal=bool(is_causal), sm_scale=None if scale is None else float(scale), pv_mode=pv_mode,
+                layout="bhnd", blk_q=blk_q, blk_k=blk_k)

@@ -75,6 +75,8 @@ def test_workspace_bytes_layout():
     (dict(blk_q=24), -1),
     (dict(blk_k=1), -1),
     (dict(blk_q=2), -1),
+    (dict(kv_heads=3), -1),
+    (dict(kv_heads=-1), -1),
     (dict(blk_k=512), -1),
     (dict(blk_k=0), -1),
     (dict(heads=0), -1),
@@ -103,6 +105,32 @@ def test_smooth_v_rejects_small_workspace_and_null_output():
     assert r == -3 and "workspace" in sage.lib().sage_last_error().decode()
     r = sage.lib().sage_quantize_v_fp8_smooth(ctypes.byref(p), FAKE, st, FAKE, st, None, FAKE, need.value, None)
     assert r == -1 and "v_scale_mean" in sage.lib().sage_last_error().decode()
+
+
+def test_gqa_workspace_counts_kv_heads():
+    # 4 query heads over 1 K/V head: int8 Q 4 heads, int8 K 1 head, Q scales 4 heads, K
+    # scales, mean and column-sum partials 1 head
+    p = _prob(heads=4, kv_heads=1)
+    rc, n = _ws(p)
+    assert rc == 0
+    # q8 4x256x64, k8 1x256x64, q scales (16 floats), k scales (4), mean (64 floats) each in a
+    # 256-byte region, 2 chunks x 64 fp64 column sums
+    assert n == 4 * 16384 + 16384 + 256 + 256 + 256 + 1024
+
+
+def test_sdpa_wrapper_rejects_what_it_does_not_do():
+    import torch
+    q = torch.zeros((1, 4, 8, 64), dtype=torch.float16)
+    kv = torch.zeros((1, 2, 8, 64), dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        sage.scaled_dot_product_attention(q, q, q, attn_mask=torch.ones(8, 8, dtype=torch.bool))
+    with pytest.raises(NotImplementedError):
+        sage.scaled_dot_product_attention(q, q, q, dropout_p=0.1)
+    with pytest.raises(ValueError):
+        sage.scaled_dot_product_attention(q, kv, kv)            # fewer K/V heads without enable_gqa
+    with pytest.raises(ValueError):
+        sage.scaled_dot_product_attention(q, torch.zeros((1, 3, 8, 64), dtype=torch.float16),
+                                          torch.zeros((1, 3, 8, 64), dtype=torch.float16), enable_gqa=True)
 
 
 def test_debug_fp8_mfma_rejects_bad_scales():
