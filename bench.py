@@ -283,7 +283,8 @@ def extra_workloads(sage, torch, dev):
              ("fp8-PV smooth-V B4 H16 N8192 d128", synth.FP8, False, 2, None),
              ("fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, None),
              ("video B2 H24 N16384 d64", synth.VIDEO, False, 0, None),
-             ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen")]
+             ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen"),
+             ("gqa causal B1 H32 kv8 N8192 d128", synth.LONG, True, 0, "gqa")]
     for name, wl, causal, mode, kind in cases:
         g.manual_seed(wl.seed)
         if kind == "varlen":
@@ -295,6 +296,10 @@ def extra_workloads(sage, torch, dev):
             cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=dev)
             kw = dict(cu_seqlens=cu, max_seqlen=int(lens.max()))
             seqlens = lens.tolist()
+        elif kind == "gqa":
+            shape = (1, 8192, wl.heads, wl.head_dim)
+            kw = {}
+            seqlens = [8192]
         else:
             shape = (wl.batch, wl.seqlen, wl.heads, wl.head_dim)
             kw = {}
@@ -303,6 +308,8 @@ def extra_workloads(sage, torch, dev):
         bias = torch.randn((wl.heads, wl.head_dim), generator=g, device=dev) * wl.bias_std
         k = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) + bias).half()
         v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
+        if kind == "gqa":                         # 8 K/V heads for the 32 query heads
+            k, v = k[:, :, :8].contiguous(), v[:, :, :8].contiguous()
         qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
         vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
         out = torch.empty_like(q)
