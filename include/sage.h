@@ -19,7 +19,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Problem.  `nseq` sequences, `heads` heads, head dimension `head_dim` (64 or
- *   128).  Dense problems (cu_seqlens == NULL) have nseq = batch and every
+ *   128; sage_attn and sage_workspace_bytes also take 96, see there; every
+ *   other entry returns SAGE_ERR_UNSUPPORTED for it).  Dense problems (cu_seqlens == NULL) have nseq = batch and every
  *   sequence of length max_seqlen.  Packed variable-length problems pass
  *   `cu_seqlens`, a DEVICE array of nseq+1 int32 prefix offsets (cu[0] = 0,
  *   non-decreasing, cu[nseq] = total_tokens); sequence s is tokens
@@ -88,7 +89,7 @@ typedef struct {
   int32_t nseq;               /* dense: batch; varlen: number of packed sequences */
   int32_t heads;
   int32_t max_seqlen;         /* dense: N; varlen: upper bound of every length    */
-  int32_t head_dim;           /* 64 or 128                                         */
+  int32_t head_dim;           /* 64 or 128 (96: sage_attn only)                    */
   int64_t total_tokens;       /* varlen: cu_seqlens[nseq]; dense: ignored          */
   const int32_t* cu_seqlens;  /* device pointer, nseq+1 entries; NULL = dense      */
   int32_t blk_q;              /* Q quantisation block (tokens)                     */
@@ -161,7 +162,12 @@ int sage_attn_quantized(const sage_problem* p,
 /* The whole forward pass: sage_quantize (+ sage_quantize_v_fp8 or
  * sage_quantize_v_fp8_smooth in the FP8 modes) into the workspace, then
  * sage_attn_quantized.  O = softmax(Q K^T * sm_scale) V
- * computed as described above.  `workspace` holds sage_workspace_bytes() bytes. */
+ * computed as described above.  `workspace` holds sage_workspace_bytes() bytes.
+ * head_dim 96 (models with 96-channel heads, [SA2] 即插即用举例): Q, K, V and
+ * O hold 96 channels per row; the intermediates in the workspace take the
+ * 128-channel layout with channels 96..127 zero (which changes no block
+ * maximum, K mean or Q.K), sm_scale <= 0 still selects 1/sqrt(96), and only
+ * channels 0..95 of O are written. */
 int sage_attn(const sage_problem* p,
               const void* Q, sage_strides qs, const void* K, sage_strides ks,
               const void* V, sage_strides vs, void* out, sage_strides os,

@@ -587,7 +587,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // row, size up to the sequence's end.
   const int8_t* knext = kseq + (int64_t)hf * BN * kn;
   const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
-  int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + 2 * D);
+  // (fp16 V rows hold dv channels: the last row is read up to them only)
+  int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
   constexpr int KL = DmaPlan<D, FP8>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8>::VPW;
@@ -857,7 +858,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
   for (int x = 0; x < BM * CPR / (NT / 2); ++x) {
     const int c = tid + x * (NT / 2), rr = c / CPR, cp = c % CPR;
-    if (q0 + rr < L)
+    if (q0 + rr < L && 8 * cp < p.dv)
       *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) =
           *(const LDS v4i*)(ostage + rr * S::OROW + 16 * cp);
   }

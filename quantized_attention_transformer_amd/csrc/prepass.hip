@@ -59,6 +59,15 @@ __device__ __forceinline__ H8 load_h8(const _Float16* p) {
   return r;
 }
 
+// 8 channels of a row, or zeros for channels past the valid ones (head_dim 96
+// runs on the 128-channel kernels with channels 96..127 zero).
+__device__ __forceinline__ H8 load_h8_or_zero(const _Float16* p, bool valid) {
+  if (valid) return load_h8(p);
+  H8 r;
+  *reinterpret_cast<uint4*>(&r) = make_uint4(0u, 0u, 0u, 0u);
+  return r;
+}
+
 // ---------------------------------------------------------------- INT8 blocks
 // The INT8 kernels run 512 threads (8 waves, two per SIMD): a text-sized head
 // gives one block per CU, and the per-element work then spreads over twice
@@ -76,12 +85,12 @@ template <int D>
 struct BlockRows {
   static constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
   H8 x[R];
-  __device__ __forceinline__ void load(const _Float16* __restrict__ src, int64_t sn, int n0, int n1) {
+  __device__ __forceinline__ void load(const _Float16* __restrict__ src, int64_t sn, int n0, int n1, bool cgv) {
     const int r = threadIdx.x / TPR;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int n = n0 + r + RPP * j;
-      if (n < n1) x[j] = load_h8(src + (int64_t)n * sn);
+      if (n < n1) x[j] = load_h8_or_zero(src + (int64_t)n * sn, cgv);
     }
   }
 };
@@ -164,7 +173,7 @@ __device__ __forceinline__ uint2 codes8(const H8& x, F transform, float scale, f
 // ones are read twice.  Returns the scale.
 template <int D, typename F>
 __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, int64_t sn, int n0, int n1,
-                                             F transform, int8_t* __restrict__ dst, int64_t dn,
+                                             F transform, int8_t* __restrict__ dst, int64_t dn, bool cgv,
                                              const BlockRows<D>* pre = nullptr) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
   const int r = threadIdx.x / TPR;
@@ -174,7 +183,7 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
     if (pre)
       rows = *pre;
     else
-      rows.load(src, sn, n0, n1);
+      rows.load(src, sn, n0, n1, cgv);
 #pragma unroll
     for (int j = 0; j < R; ++j)
       if (n0 + r + RPP * j < n1) ex.add(rows.x[j]);
@@ -191,14 +200,14 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
     return scale;
   }
 #pragma unroll 2
-  for (int n = n0 + r; n < n1; n += RPP) ex.add(load_h8(src + (int64_t)n * sn));
+  for (int n = n0 + r; n < n1; n += RPP) ex.add(load_h8_or_zero(src + (int64_t)n * sn, cgv));
   const float a = block_max<kQThreads>(n0 + r < n1 ? ex.absmax(transform) : 0.0f);
   const float scale = a > 0.0f ? a / 127.0f : 0.0f;
   const float y = __builtin_amdgcn_rcpf(scale);
 #pragma unroll 2
   for (int n = n0 + r; n < n1; n += RPP)
     *reinterpret_cast<uint2*>(dst + (int64_t)n * dn) =
-        a > 0.0f ? codes8(load_h8(src + (int64_t)n * sn), transform, scale, y) : make_uint2(0u, 0u);
+        a > 0.0f ? codes8(load_h8_or_zero(src + (int64_t)n * sn, cgv), transform, scale, y) : make_uint2(0u, 0u);
   return scale;
 }
 
@@ -211,13 +220,14 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
-    int max_seqlen, int blk_q, int nbq, int nqw, int nks, int kv_heads, float sm_scale, int8_t* __restrict__ q8,
-    Str q8s,
+    int max_seqlen, int blk_q, int nbq, int nqw, int nks, int kv_heads, int dv, float sm_scale,
+    int8_t* __restrict__ q8, Str q8s,
     float* __restrict__ sq, double* __restrict__ part) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int L = seq_len(cu, s, max_seqlen);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const bool cgv = 8 * cg < dv;  // this thread's 8 channels are real (not head_dim 96 padding)
   const int64_t sh = (int64_t)s * H + h;
   auto scale_q = [&](float v, int) { return v * sm_scale; };
   if (x < nqw && blk_q == 1) {
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     H8 row;
     float a = 0.0f;
     if (valid) {
-      row = load_h8(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8);
+      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8, cgv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf((float)row.v[i]));
       a *= sm_scale;
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     if (n0 >= L) return;
     const int n1 = min(L, n0 + blk_q);
     const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, scale_q,
-                                       q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n);
+                                       q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n, cgv);
     if (tid == 0) sq[sh * nbq + x] = scale;
     return;
   }
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
   static_assert(kKSumRows <= 128, "a chunk fits the register-cached rows");
   {
     BlockRows<D> krows;
-    krows.load(kb, ks.n, n0, n1);
+    krows.load(kb, ks.n, n0, n1, cgv);
 #pragma unroll
     for (int j = 0; j < BlockRows<D>::R; ++j)
       if (n0 + r + RPP * j < n1)
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __res
 template <int D, bool FOLD>
 __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
                                                        const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
-                                                       int nbk, int nks, const double* __restrict__ part,
+                                                       int nbk, int nks, int dv, const double* __restrict__ part,
                                                        float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
                                                        float* __restrict__ sk) {
   constexpr int TPR = D / 8;
@@ -340,9 +350,10 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
   const int cg = threadIdx.x % TPR;
   const int64_t sh = (int64_t)s * H + h;
   const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
+  const bool cgv = 8 * cg < dv;
   BlockRows<D> krows;
   const bool pre = n1 - n0 <= 128;
-  if (pre) krows.load(kb, ks.n, n0, n1);
+  if (pre) krows.load(kb, ks.n, n0, n1, cgv);
   float mean[8];
   if constexpr (FOLD) {
     __shared__ float kmean[D];
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
     for (int i = 0; i < 8; ++i) mean[i] = km[sh * D + cg * 8 + i];
   }
   const float scale = quant_block<D>(kb, ks.n, n0, n1, [&](float v, int i) { return v - mean[i]; },
-                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n, pre ? &krows : nullptr);
+                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n, cgv, pre ? &krows : nullptr);
   if (threadIdx.x == 0) sk[sh * nbk + bi] = scale;
 }
 
@@ -378,7 +389,7 @@ __global__ void k_fill_zero(float* __restrict__ x, int64_t n) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_colmax(const _Float16* __restrict__ V, Str vs,
-                                                        const int32_t* __restrict__ cu, int max_seqlen,
+                                                        const int32_t* __restrict__ cu, int max_seqlen, int dv,
                                                         float* __restrict__ vmax) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
   const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void k_v_colmax(const _Float16* __restric
   float m[8] = {};
 #pragma unroll 4
   for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(base + (int64_t)n * vs.n);
+    H8 x = load_h8_or_zero(base + (int64_t)n * vs.n, 8 * cg < dv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf((float)x.v[i]));
   }
@@ -415,7 +426,7 @@ __global__ void k_v_scale(float* __restrict__ sv, int64_t n) {
 // fp32(V - vmean), the smoothed V) with the per-channel scales sv.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict__ V, Str vs,
-                                                       const int32_t* __restrict__ cu, int max_seqlen,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int dv,
                                                        const float* __restrict__ sv,
                                                        const float* __restrict__ vmean, uint8_t* __restrict__ v8,
                                                        Str v8s) {
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
   }
 #pragma unroll 2
   for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8(src + (int64_t)n * vs.n);
+    H8 x = load_h8_or_zero(src + (int64_t)n * vs.n, 8 * cg < dv);
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = scale[i] > 0.0f ? ((float)x.v[i] - mean[i]) / scale[i] : 0.0f;
@@ -459,7 +470,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
 // channel, the exact fp64 sum and the fp16 maximum and minimum (as float).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restrict__ V, Str vs,
-                                                          const int32_t* __restrict__ cu, int max_seqlen, int nchunk,
+                                                          const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                          int nchunk,
                                                           double* __restrict__ psum, float* __restrict__ pmax,
                                                           float* __restrict__ pmin) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restr
   Extremes ex;
 #pragma unroll 4
   for (int n = n0 + r; n < n1; n += RPP) {
-    const H8 x = load_h8(base + (int64_t)n * vs.n);
+    const H8 x = load_h8_or_zero(base + (int64_t)n * vs.n, 8 * cg < dv);
     ex.add(x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
@@ -560,7 +572,7 @@ hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const 
     const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
     hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st,
                        (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.nbq, nqw,
-                       p.nks, p.kv_heads, sm_scale, q8, q8s, q_scale, partial);
+                       p.nks, p.kv_heads, p.dv, sm_scale, q8, q8s, q_scale, partial);
   });
   return hipGetLastError();
 }
@@ -571,7 +583,7 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
   if (p.nks <= kFoldMaxBlocks) {
     SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
                                                    (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
-                                                   partial, k_mean, k8, k8s, k_scale));
+                                                   p.dv, partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
@@ -580,7 +592,7 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
                                                  (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
-                                                 partial, k_mean, k8, k8s, k_scale));
+                                                 p.dv, partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
 }
 
@@ -589,7 +601,7 @@ hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* vmax,
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vmax, n);
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colmax<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, vmax));
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, vmax));
   return hipGetLastError();
 }
 
@@ -603,8 +615,8 @@ hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* 
                           uint8_t* v8, Str v8s, hipStream_t st) {
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_v<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, v_scale, v_mean, v8,
-                                                 v8s));
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, v_scale, v_mean,
+                                                 v8, v8s));
   return hipGetLastError();
 }
 
@@ -612,8 +624,8 @@ hipError_t launch_v_smooth_stats(const Problem& p, const void* V, Str vs, double
                                  float* v_scale, float* v_mean, hipStream_t st) {
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colstats<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.nchunk, psum, pmax,
-                                                 pmin));
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, p.nchunk, psum,
+                                                 pmax, pmin));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(D), 0, st, psum,

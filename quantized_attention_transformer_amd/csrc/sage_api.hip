@@ -35,13 +35,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-int check_problem(const sage_problem* p) {
+// head_dim 96 runs on the 128-channel kernels with channels 96..127 zero; it is
+// accepted by the entries that own their int8/E4M3 intermediates (sage_attn and
+// its workspace query), whose layout then stays internal.
+int check_problem(const sage_problem* p, bool allow_d96 = false) {
   if (!p) return fail(SAGE_ERR_INVALID_ARG, "problem is NULL");
   if (p->nseq < 0 || p->heads <= 0 || p->max_seqlen < 0)
     return fail(SAGE_ERR_INVALID_ARG, "nseq (%d) must be >= 0, heads (%d) > 0, max_seqlen (%d) >= 0", p->nseq,
                 p->heads, p->max_seqlen);
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if (p->head_dim == 96 && !allow_d96)
+    return fail(SAGE_ERR_UNSUPPORTED, "head_dim 96 is supported by sage_attn only (this entry: 64 or 128)");
+  if (p->head_dim != 64 && p->head_dim != 96 && p->head_dim != 128)
+    return fail(SAGE_ERR_UNSUPPORTED, "head_dim %d not supported (64, 96 or 128)", p->head_dim);
   auto block_ok = [](int b) { return b >= 16 && b <= 256 && b % 16 == 0; };
   if (!(block_ok(p->blk_q) || p->blk_q == 1) || !block_ok(p->blk_k))
     return fail(SAGE_ERR_INVALID_ARG,
@@ -64,7 +69,8 @@ sage::Problem to_internal(const sage_problem* p) {
   q.heads = p->heads;
   q.kv_heads = p->kv_heads > 0 ? p->kv_heads : p->heads;
   q.max_seqlen = p->max_seqlen;
-  q.head_dim = p->head_dim;
+  q.head_dim = p->head_dim == 96 ? 128 : p->head_dim;
+  q.dv = p->head_dim;
   q.blk_q = p->blk_q;
   q.blk_k = p->blk_k;
   q.nbq = (int)cdiv(p->max_seqlen, p->blk_q);
@@ -118,7 +124,7 @@ struct VSmoothWs {
 
 VSmoothWs v_smooth_ws(const sage_problem* p, size_t base) {
   const sage::Problem q = to_internal(p);
-  const size_t n = (size_t)p->nseq * q.kv_heads * q.nchunk * p->head_dim;
+  const size_t n = (size_t)p->nseq * q.kv_heads * q.nchunk * q.head_dim;
   VSmoothWs w{};
   w.psum = base;
   w.pmax = w.psum + align_up(n * 8);
@@ -130,7 +136,7 @@ VSmoothWs v_smooth_ws(const sage_problem* p, size_t base) {
 WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   const sage::Problem q = to_internal(p);
   const int64_t T = tokens(p);
-  const int64_t d = p->head_dim, H = p->heads, Hk = q.kv_heads;
+  const int64_t d = q.head_dim, H = p->heads, Hk = q.kv_heads;
   WsLayout w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -169,7 +175,7 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
 
 size_t quantize_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
-  return align_up((size_t)p->nseq * q.kv_heads * q.nks * p->head_dim * 8);
+  return align_up((size_t)p->nseq * q.kv_heads * q.nks * q.head_dim * 8);
 }
 
 int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
@@ -201,7 +207,7 @@ int run_quantize_v(const sage_problem* p, const void* V, sage_strides vs, uint8_
 int run_quantize_v_smooth(const sage_problem* p, const void* V, sage_strides vs, uint8_t* v8, sage_strides v8s,
                           float* v_scale_mean, char* ws, const VSmoothWs& w, hipStream_t st) {
   const sage::Problem q = to_internal(p);
-  float* const vmean = v_scale_mean + (size_t)p->nseq * kv_heads_of(p) * p->head_dim;
+  float* const vmean = v_scale_mean + (size_t)p->nseq * q.kv_heads * q.head_dim;
   hipError_t e;
   if ((e = sage::launch_v_smooth_stats(q, V, S(vs), (double*)(ws + w.psum), (float*)(ws + w.pmax),
                                        (float*)(ws + w.pmin), v_scale_mean, vmean, st)) != hipSuccess)
@@ -218,7 +224,7 @@ extern "C" {
 const char* sage_last_error(void) { return g_last_error.c_str(); }
 
 int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes) {
-  int rc = check_problem(p);
+  int rc = check_problem(p, true);
   if (rc) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
@@ -307,7 +313,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
 int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks, const void* V,
               sage_strides vs, void* out, sage_strides os, int causal, float sm_scale, int pv_mode, void* workspace,
               size_t workspace_bytes, void* stream) {
-  int rc = check_problem(p);
+  int rc = check_problem(p, true);
   if (rc) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
@@ -339,7 +345,7 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
     const VSmoothWs vw{w.vpsum, w.vpmax, w.vpmin, 0};
     if ((rc = run_quantize_v_smooth(p, V, vs, (uint8_t*)(ws + w.v8), w.s8kv, (float*)(ws + w.sv), ws, vw, st)))
       return rc;
-    vmean = (const float*)(ws + w.sv) + (size_t)p->nseq * kv_heads_of(p) * p->head_dim;
+    vmean = (const float*)(ws + w.sv) + (size_t)p->nseq * kv_heads_of(p) * to_internal(p).head_dim;
   }
   if (pv_mode != SAGE_PV_FP16) {
     vin = ws + w.v8;

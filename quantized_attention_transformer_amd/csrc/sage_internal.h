@@ -31,6 +31,8 @@ struct Problem {
   const int32_t* cu;
   int nseq, heads, max_seqlen, head_dim, blk_q, blk_k;
   int kv_heads;          // heads of K and V (grouped-query attention: heads % kv_heads == 0)
+  int dv;                // channels of the fp16 inputs and of O: head_dim, or 96 with head_dim 128
+                         // (head dimension 96 runs on the 128-channel kernels, channels 96..127 zero)
   int nbq, nbk, nchunk;  // ceil(max_seqlen/blk_q), ceil(max_seqlen/blk_k), ceil(max_seqlen/kColChunk)
   int nks;               // ceil(max_seqlen/kKSumRows): K column-sum partials per (sequence, head)
 };

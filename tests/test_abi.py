@@ -70,7 +70,7 @@ def test_workspace_bytes_layout():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=96), -2),
+    (dict(head_dim=80), -2),
     (dict(head_dim=0), -2),
     (dict(blk_q=24), -1),
     (dict(blk_k=1), -1),
@@ -116,6 +116,24 @@ def test_gqa_workspace_counts_kv_heads():
     # q8 4x256x64, k8 1x256x64, q scales (16 floats), k scales (4), mean (64 floats) each in a
     # 256-byte region, 2 chunks x 64 fp64 column sums
     assert n == 4 * 16384 + 16384 + 256 + 256 + 256 + 1024
+
+
+def test_head_dim_96_runs_on_the_128_channel_layout():
+    # sage_attn owns its intermediates: at head_dim 96 they take the 128-channel layout
+    for mode in (0, 1, 2):
+        for kw in (dict(), dict(heads=4, kv_heads=2), dict(blk_q=1)):
+            rc96, n96 = _ws(_prob(head_dim=96, **kw), mode)
+            rc128, n128 = _ws(_prob(head_dim=128, **kw), mode)
+            assert rc96 == 0 and rc128 == 0 and n96 == n128, (mode, kw)
+    # entries whose int8/E4M3 outputs the caller lays out take 64 or 128 only
+    m = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_workspace_bytes(ctypes.byref(_prob(head_dim=96)), ctypes.byref(m)) == -2
+    assert "96" in sage.lib().sage_last_error().decode()
+    assert sage.lib().sage_quantize_v_fp8_smooth_workspace_bytes(ctypes.byref(_prob(head_dim=96)),
+                                                                 ctypes.byref(m)) == -2
+    st = _strides()
+    p = _prob(head_dim=96)
+    assert sage.lib().sage_quantize_v_fp8(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, None) == -2
 
 
 def test_sdpa_wrapper_rejects_what_it_does_not_do():
