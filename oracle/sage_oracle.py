@@ -52,6 +52,14 @@ Steps, in the pages' order:
     448 / l with l from the unquantised p.  E4M3 is the OCP format (bias 7, max 448, no
     infinities), round-to-nearest-even, saturating at 448.
 
+Smooth Q ([SA2] 技术方案 item 1, optional here as on the page's INT8
+kernel): mean(Q') per channel over the tokens of the sequence (the same
+reading as mean(K)), taken from the exact fp64 sum of the fp16 Q as
+fp32((sum / L) * sm_scale); Q_s = fp32(Q' - mean(Q')) is quantised in place
+of Q'; the product of mean(Q') with K_s^T, one value per key (delta_j =
+mean(Q') . K_s[j] in fp64), is added to every row of S in step 6, which
+makes S equal to Q' K_s^T again up to quantisation.
+
 K and V may have fewer heads than Q (grouped-query attention, which the
 scaled-dot-product-attention interface the pages' drop-in replaces accepts):
 query head h reads K/V head h // (Hq / Hk), and K's mean is per K head.
@@ -105,6 +113,29 @@ def fold_sm_scale(q_seq: np.ndarray, sm_scale) -> np.ndarray:
     return q_seq.astype(np.float32) * np.float32(sm_scale)
 
 
+def q_mean(q_seq: np.ndarray, sm_scale) -> np.ndarray:
+    """mean(Q') over the tokens of one sequence, per channel, for smoothing Q
+    ([SA2] 技术方案 item 1).  q_seq: fp16 [L, d].  Exact fp64 sum of the fp16
+    values, then fp32((sum / L) * sm_scale) with fp64 operations (mean(Q * s)
+    = mean(Q) * s, taken so that the sum stays exact)."""
+    L = q_seq.shape[0]
+    if L == 0:
+        return np.zeros(q_seq.shape[1], np.float32)
+    s = np.sum(q_seq.astype(np.float64), axis=0)
+    return ((s / np.float64(L)) * np.float64(np.float32(sm_scale))).astype(np.float32)
+
+
+def smooth_q_values(q_fold: np.ndarray, qm: np.ndarray) -> np.ndarray:
+    """Q_s = fp32(Q' - mean(Q')) for Q' = fold_sm_scale(Q) ([SA2] 技术方案 item 1)."""
+    return (q_fold.astype(np.float32) - qm.astype(np.float32)[None, :]).astype(np.float32)
+
+
+def q_delta(qm: np.ndarray, k_s: np.ndarray) -> np.ndarray:
+    """The compensation of smoothing Q: mean(Q') . K_s^T, one value per key
+    ([SA2] 技术方案 item 1: a vector-matrix product added to S).  fp64 [L]."""
+    return k_s.astype(np.float64) @ qm.astype(np.float64)
+
+
 def quant_block(x: np.ndarray):
     """INT8 quantisation of one block with one scale ([SA] 技术方案, per-block
     INT8 quantisation of Q and K).  x: fp32 [rows, d].  Returns (int8 codes,
@@ -140,7 +171,7 @@ def _seq_views(x: np.ndarray, cu: Optional[np.ndarray], nseq: int):
 
 
 def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Optional[np.ndarray],
-                blk_q: int, blk_k: int, sm_scale=None, smooth: bool = True):
+                blk_q: int, blk_k: int, sm_scale=None, smooth: bool = True, smooth_q: bool = False):
     """Steps 1-4 for every (sequence, head).
 
     q, k: fp16 in [B, N, H, d] (dense, cu None) or [T, H, d] (packed, cu int32
@@ -149,7 +180,10 @@ def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Option
     layout as the input), sq [nseq, Hq, ceil(maxL/blk_q)], sk [nseq, Hk,
     ceil(maxL/blk_k)] (entries past a sequence's last block are 0) and km
     [nseq, Hk, d] fp32 (the mean is per K head).  smooth=False is the ablation
-    without mean subtraction (km is then 0)."""
+    without mean subtraction (km is then 0).  smooth_q: Q is smoothed too;
+    adds qm [nseq, Hq, d] fp32 (mean(Q')) and qdelta [nseq, Hq, maxL] fp64
+    (mean(Q') . K_s^T per key; 0 past a sequence's end), and q8/sq are those
+    of Q_s."""
     nseq = len(seqlens)
     H, d = q.shape[-2], q.shape[-1]
     Hk = k.shape[-2]
@@ -160,10 +194,14 @@ def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Option
     sq = np.zeros((nseq, H, -(-maxL // blk_q)), np.float32)
     sk = np.zeros((nseq, Hk, -(-maxL // blk_k)), np.float32)
     km = np.zeros((nseq, Hk, d), np.float32)
+    qm = np.zeros((nseq, H, d), np.float32)
+    qdel = np.zeros((nseq, H, maxL), np.float64)
+    grp = H // Hk
     qv, kv = _seq_views(q, cu, nseq), _seq_views(k, cu, nseq)
     q8v, k8v = _seq_views(q8, cu, nseq), _seq_views(k8, cu, nseq)
     for s in range(nseq):
         L = int(seqlens[s])
+        k_s = []
         for h in range(Hk):
             kh = kv[s][:L, h, :]
             if smooth:
@@ -171,14 +209,23 @@ def quantize_qk(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Option
                 ks = smooth_k(kh, km[s, h])
             else:
                 ks = kh.astype(np.float32)
+            k_s.append(ks)
             c, sc = quant_rows(ks, blk_k)
             k8v[s][:L, h, :] = c
             sk[s, h, :len(sc)] = sc
         for h in range(H):
-            c, sc = quant_rows(fold_sm_scale(qv[s][:L, h, :], sm), blk_q)
+            qf = fold_sm_scale(qv[s][:L, h, :], sm)
+            if smooth_q:
+                qm[s, h] = q_mean(qv[s][:L, h, :], sm)
+                qf = smooth_q_values(qf, qm[s, h])
+                qdel[s, h, :L] = q_delta(qm[s, h], k_s[h // grp])
+            c, sc = quant_rows(qf, blk_q)
             q8v[s][:L, h, :] = c
             sq[s, h, :len(sc)] = sc
-    return dict(q8=q8, k8=k8, sq=sq, sk=sk, km=km, sm_scale=sm)
+    out = dict(q8=q8, k8=k8, sq=sq, sk=sk, km=km, sm_scale=sm)
+    if smooth_q:
+        out.update(qm=qm, qdelta=qdel)
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -294,11 +341,12 @@ def fp8_probs(S):
 
 
 def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
-                   pv_fp8=False, v8h=None, svh=None, return_lse=False, vmh=None):
+                   pv_fp8=False, v8h=None, svh=None, return_lse=False, vmh=None, qdel=None):
     """One (sequence, head).  q8h, k8h: int8 [L, d]; sqh, skh: per-block scales;
     vh: fp16 [L, d]; rows: query indices to compute (default all); FP8 path:
     v8h, svh and, with smooth V, vmh (the mean added back to O: every row of
-    P sums to 1, so P V = P (V - mean) + mean).
+    P sums to 1, so P V = P (V - mean) + mean); smooth Q: qdel [L], the
+    per-key compensation mean(Q') . K_s^T added to every row of S.
     Returns O fp64 [len(rows), d]."""
     L = q8h.shape[0]
     rows = np.arange(L) if rows is None else np.asarray(rows)
@@ -308,6 +356,8 @@ def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
     rs = sqh[rows // blk_q].astype(np.float64)
     cs = skh[np.arange(L) // blk_k].astype(np.float64)
     S = s_int.astype(np.float64) * rs[:, None] * cs[None, :]         # step 6
+    if qdel is not None:
+        S = S + np.asarray(qdel, np.float64)[None, :L]
     if causal:
         S = np.where(np.arange(L)[None, :] <= rows[:, None], S, -np.inf)
     m = np.max(S, axis=1, keepdims=True)                             # step 7
@@ -328,17 +378,17 @@ def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
 
 
 def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=False,
-              rows_by_seq=None, smooth=True, quant=None, smooth_v=False):
+              rows_by_seq=None, smooth=True, quant=None, smooth_v=False, smooth_q=False):
     """The whole forward pass.  Layouts as in quantize_qk.  rows_by_seq
     optionally maps a sequence index to the query rows to compute (the rest
     of O is left NaN).  smooth_v (FP8 path): subtract mean(V) before the E4M3
-    quantisation and add it to O.  Returns (O fp64 in Q's layout,
-    quantisation dict)."""
+    quantisation and add it to O.  smooth_q: smooth Q as well (quantize_qk).
+    Returns (O fp64 in Q's layout, quantisation dict)."""
     nseq = len(seqlens)
     H = q.shape[-2]
     grp = H // k.shape[-2]  # query heads per K/V head (grouped-query attention)
     qd = quant if quant is not None else quantize_qk(q, k, seqlens, cu, blk_q, blk_k, sm_scale,
-                                                     smooth=smooth)
+                                                     smooth=smooth, smooth_q=smooth_q)
     if pv_fp8:
         v8, sv, vm = quant_v_fp8(v, seqlens, cu, smooth_v)
         qd = dict(qd, v8=v8, sv=sv, vm=vm)
@@ -357,7 +407,8 @@ def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=
                                vv[s][:L, kh], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8,
                                v8h=None if v8v is None else v8v[s][:L, kh],
                                svh=None if v8v is None else qd["sv"][s, kh],
-                               vmh=qd["vm"][s, kh] if (pv_fp8 and smooth_v) else None)
+                               vmh=qd["vm"][s, kh] if (pv_fp8 and smooth_v) else None,
+                               qdel=qd["qdelta"][s, h, :L] if "qdelta" in qd else None)
             if rows is None:
                 ov[s][:L, h] = o
             else:

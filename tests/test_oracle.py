@@ -476,3 +476,118 @@ def test_gqa_equals_repeated_kv_heads(hk):
             np.testing.assert_array_equal(qg["k8"], qm["k8"][:, :, ::H // hk])
         np.testing.assert_array_equal(O.exact_attention(q, k, v, [L], None, causal),
                                       O.exact_attention(q, rep(k), rep(v), [L], None, causal))
+
+
+# ---------------------------------------------------------------- smooth Q
+
+def _smooth_q_example():
+    g = GOLD["ex_g_smooth_q"]
+    q = np.array(g["q"], np.float16)[None, :, None, :]
+    k = np.array(g["k"], np.float16)[None, :, None, :]
+    v = np.array(g["v"], np.float16)[None, :, None, :]
+    return g, q, k, v
+
+
+def test_ex_g_smooth_q():
+    g, q, k, v = _smooth_q_example()
+    o, qd = O.sage_attn(q, k, v, [2], None, False, 2, 2, sm_scale=g["sm_scale"], smooth_q=True)
+    np.testing.assert_array_equal(qd["qm"][0, 0], np.array(g["q_mean"], np.float32))
+    np.testing.assert_array_equal(qd["q8"][0, :, 0], np.array(g["q_codes"], np.int8))
+    assert hex(int(qd["sq"][0, 0, 0:1].view(np.uint32)[0])) == g["q_scale_bits"]
+    np.testing.assert_array_equal(qd["k8"][0, :, 0], np.array(g["k_codes"], np.int8))
+    np.testing.assert_array_equal(qd["qdelta"][0, 0], np.array(g["delta"], np.float64))
+    s = (qd["q8"][0, :, 0].astype(np.float64) @ qd["k8"][0, :, 0].astype(np.float64).T) \
+        * float(qd["sq"][0, 0, 0]) * float(qd["sk"][0, 0, 0]) + qd["qdelta"][0, 0][None, :]
+    np.testing.assert_allclose(s, np.array(g["scores"], np.float64), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(o[0, :, 0], np.array(g["o"], np.float64), rtol=0, atol=1e-6)
+    # exact re-derivation: mean = RN32(sum / L * sm), Q_s = RN32(RN32(Q sm) - mean), block codes
+    qq = [[Fraction(float(x)) for x in row] for row in q[0, :, 0]]
+    sm = Fraction(g["sm_scale"])
+    mean = [rn32((qq[0][c] + qq[1][c]) / 2 * sm) for c in range(4)]
+    assert mean == [Fraction(float(x)) for x in qd["qm"][0, 0]]
+    qs = [rn32(rn32(x * sm) - mean[c]) for row in qq for c, x in enumerate(row)]
+    codes, sc = exact_quant_block(qs)
+    assert codes == [int(x) for x in qd["q8"][0, :, 0].ravel()]
+    assert sc == Fraction(float(qd["sq"][0, 0, 0]))
+
+
+def test_smooth_q_with_zero_mean_q_is_the_plain_method():
+    # tokens in +- pairs: the channel sums are exactly 0, so mean(Q') = 0, Q_s = Q' and
+    # the compensation vanishes
+    rng = np.random.default_rng(51)
+    L, H, d = 96, 2, 64
+    half = rng.standard_normal((1, L // 2, H, d)).astype(np.float16)
+    q = np.concatenate([half, -half], axis=1)
+    k = (rng.standard_normal((1, L, H, d)) + 3 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    for causal in (False, True):
+        a, qa = O.sage_attn(q, k, v, [L], None, causal, 32, 16)
+        b, qb = O.sage_attn(q, k, v, [L], None, causal, 32, 16, smooth_q=True)
+        assert not qb["qm"].any() and not qb["qdelta"].any()
+        np.testing.assert_array_equal(qa["q8"], qb["q8"])
+        np.testing.assert_array_equal(a, b)
+
+
+def test_smooth_q_constant_rows_give_exact_attention():
+    # every token of a head equal: Q_s = 0 (codes 0, scale 0), so S is the compensation
+    # alone, mean(Q') . K_s^T = Q' K_s^T, and softmax(Q' K_s^T) = softmax(Q' K^T * s):
+    # nothing of Q is quantised; only fp32 roundings of Q' and K_s remain
+    rng = np.random.default_rng(52)
+    L, H, d = 120, 2, 64
+    row = rng.standard_normal((1, 1, H, d)).astype(np.float16)
+    q = np.broadcast_to(row, (1, L, H, d)).copy()
+    k = (rng.standard_normal((1, L, H, d)) + 2 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    for causal in (False, True):
+        ref = O.exact_attention(q, k, v, [L], None, causal)
+        o, qd = O.sage_attn(q, k, v, [L], None, causal, 64, 64, smooth_q=True)
+        assert not qd["q8"].any() and not qd["sq"].any()
+        np.testing.assert_allclose(o, ref, rtol=0, atol=2e-6)
+        plain, _ = O.sage_attn(q, k, v, [L], None, causal, 64, 64)
+        assert np.abs(plain - ref).max() > 50 * np.abs(o - ref).max()
+
+
+def test_smooth_q_helps_channels_with_an_offset():
+    # Q with a large per-channel offset: per-block INT8 spends its levels on the offset
+    rng = np.random.default_rng(53)
+    L, H, d = 256, 2, 64
+    q = (rng.standard_normal((1, L, H, d)) + 6 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    k = (rng.standard_normal((1, L, H, d)) + 2 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    ref = O.exact_attention(q, k, v, [L], None, False)
+    o_plain, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64)
+    o_smooth, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64, smooth_q=True)
+    rms = lambda o: float(np.sqrt(np.mean((o - ref) ** 2)))  # noqa: E731
+    assert rms(o_smooth) < 0.5 * rms(o_plain)
+    assert cos(o_smooth, ref) > cos(o_plain, ref)
+
+
+def test_smooth_q_delta_is_the_product_of_the_mean_and_smoothed_k():
+    # delta_j = mean(Q') . K_s[j]: brute force over the channels in exact rationals
+    rng = np.random.default_rng(54)
+    L, H, d = 9, 2, 8
+    q = (rng.standard_normal((1, L, H, d)) + 2).astype(np.float16)
+    k = rng.standard_normal((1, L, 1, d)).astype(np.float16)
+    qd = O.quantize_qk(q, k, [L], None, 4, 16, smooth_q=True)
+    for h in range(H):
+        qm = [Fraction(float(x)) for x in qd["qm"][0, h]]
+        km = qd["km"][0, 0]
+        for j in range(L):
+            ks = [Fraction(float(np.float32(np.float32(k[0, j, 0, c]) - km[c]))) for c in range(d)]
+            want = float(sum(a * b for a, b in zip(qm, ks)))
+            assert abs(qd["qdelta"][0, h, j] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+@pytest.mark.parametrize("hk", [1, 2])
+def test_smooth_q_gqa_equals_repeated_kv_heads(hk):
+    rng = np.random.default_rng(55)
+    L, H, d = 70, 4, 64
+    q = (rng.standard_normal((1, L, H, d)) + 3 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    k = (rng.standard_normal((1, L, hk, d)) + 3 * rng.standard_normal((1, 1, hk, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, hk, d)).astype(np.float16)
+    rep = lambda x: np.repeat(x, H // hk, axis=2)  # noqa: E731
+    for causal in (False, True):
+        og, qg = O.sage_attn(q, k, v, [L], None, causal, 32, 64, smooth_q=True)
+        om, qm = O.sage_attn(q, rep(k), rep(v), [L], None, causal, 32, 64, smooth_q=True)
+        np.testing.assert_array_equal(og, om)
+        np.testing.assert_array_equal(qg["qdelta"], qm["qdelta"])
