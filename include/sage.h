@@ -97,12 +97,16 @@ typedef struct {
   int32_t kv_heads;           /* heads of K and V; 0 = heads.  Fewer (a divisor of
                                  heads): grouped-query attention, query head h
                                  reads K/V head h / (heads / kv_heads)            */
+  int32_t smooth_q;           /* 1: smooth Q as well (sage_attn and
+                                 sage_quantize_smooth_q; blk_k a multiple of 64);
+                                 0: not                                           */
 } sage_problem;
 
 /* Bytes of workspace sage_attn and sage_quantize need for this problem
  * (sage_attn: int8 Q/K, their scales, mean(K), column-sum partials and, for
  * the FP8 modes, the E4M3 V, its scales (and means and column statistics
- * for SAGE_PV_FP8_SMOOTH_V); sage_quantize: the column-sum
+ * for SAGE_PV_FP8_SMOOTH_V); with smooth_q also Q's column-sum partials,
+ * mean(Q') and the per-key compensation; sage_quantize: the column-sum
  * partials only).  Writes *bytes; returns SAGE_OK or SAGE_ERR_INVALID_ARG. */
 int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes);
 int sage_quantize_workspace_bytes(const sage_problem* p, size_t* bytes);
@@ -120,6 +124,27 @@ int sage_quantize(const sage_problem* p,
                   int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s,
                   float* q_scale, float* k_scale, float* k_mean,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* sage_quantize with Q smoothed as well ([SA2] 技术方案 item 1; p->smooth_q
+ * must be 1, blk_k a multiple of 64):
+ *   q_mean[s][h][c] = fp32( ((sum over the sequence's tokens of Q, exact) / L)
+ *                           * sm_scale )                       (fp64 operations)
+ *   Q_s = fp32(fp32(Q * sm_scale) - q_mean), quantised per block (or per
+ *   token) in place of Q' as above; K as in sage_quantize;
+ *   q_delta[s][h][n] = fp32( sum_c q_mean[s][h][c] * K'[s][h'][n][c] ), the
+ *   sum in fp64 (h' = the K head of query head h), which sage_attn adds to
+ *   every row of S: S = q8 . k8 * q_scale * k_scale + q_delta.
+ * q_mean: [nseq][heads][head_dim] fp32.  q_delta: fp32, dense
+ * [nseq][heads][max_seqlen], packed [heads][total_tokens] (entries past a
+ * sequence's end unspecified).  `workspace` holds
+ * sage_quantize_smooth_q_workspace_bytes() bytes (column-sum partials of Q
+ * and K). */
+int sage_quantize_smooth_q_workspace_bytes(const sage_problem* p, size_t* bytes);
+int sage_quantize_smooth_q(const sage_problem* p,
+                           const void* Q, sage_strides qs, const void* K, sage_strides ks, float sm_scale,
+                           int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s,
+                           float* q_scale, float* k_scale, float* k_mean, float* q_mean, float* q_delta,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* FP8 E4M3 V for the FP8 P.V path ([SA2] 技术方案 item 4):
  *   v_scale[s][h][c] = fp32(max over the sequence's tokens of |V| / 448)
@@ -152,7 +177,8 @@ int sage_quantize_v_fp8_smooth(const sage_problem* p, const void* V, sage_stride
  *   of the smoothed V and v_scale points to the scales followed by the means
  *   (as written by sage_quantize_v_fp8_smooth); the epilogue adds the mean,
  *   exact since every row of softmax(S) sums to 1.  O is written as fp16 with
- *   strides os; rows of a sequence of length 0 are not written. */
+ *   strides os; rows of a sequence of length 0 are not written.  Problems
+ *   with smooth_q set go through sage_attn (SAGE_ERR_UNSUPPORTED here). */
 int sage_attn_quantized(const sage_problem* p,
                         const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
                         const float* q_scale, const float* k_scale,
@@ -167,7 +193,10 @@ int sage_attn_quantized(const sage_problem* p,
  * O hold 96 channels per row; the intermediates in the workspace take the
  * 128-channel layout with channels 96..127 zero (which changes no block
  * maximum, K mean or Q.K), sm_scale <= 0 still selects 1/sqrt(96), and only
- * channels 0..95 of O are written. */
+ * channels 0..95 of O are written.
+ * smooth_q = 1: sage_quantize_smooth_q in place of sage_quantize, and the
+ * fused kernel adds q_delta to S (a block whose scale is 0 has all codes 0;
+ * its S is then the compensation alone). */
 int sage_attn(const sage_problem* p,
               const void* Q, sage_strides qs, const void* K, sage_strides ks,
               const void* V, sage_strides vs, void* out, sage_strides os,

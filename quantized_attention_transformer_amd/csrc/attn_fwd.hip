@@ -62,6 +62,17 @@
 // 2^(m - m0).  l sums the fp32 P before rounding (fp32 adds), except on the
 // fp16 path at D = 64, where it sums the fp16-rounded P fed to the MFMA
 // (v_dot2).
+//
+// Smooth Q ("4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级",
+// section 技术方案 item 1; key blocks that are multiples of 64): S gains the
+// per-key compensation delta_j = mean(Q') . K_s[j].  The half that loads K(t)
+// also loads delta(t) (256 bytes) into a ring of 6 LDS slots, read by the
+// softmax of tile t; there x' = fma(delta_j, 1/(qs ks), x) puts delta_j in
+// units of the integer scores (x stays the exact float 1.5*2^23 + S, and
+// x' c = S c + delta_j log2(e)), before the row maximum.  A zero Q or K block
+// scale (all codes 0: S is the compensation alone) is replaced by a positive
+// one (2^-40 for Q, so that delta keeps fp32 precision in x'; 1 for K, where
+// delta is 0).
 #include <type_traits>
 
 #include "sage_internal.h"
@@ -73,6 +84,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
@@ -118,6 +130,11 @@ struct Lds {
   static constexpr int OROW = 2 * D + 16;
   static constexpr int OSTAGE = MERGE;
   static_assert(OSTAGE + BM * OROW <= BYTES, "O staging fits the workgroup's LDS");
+  // smooth Q: ring of NSD slots of 1 KiB past BYTES, each holding 4 copies of
+  // one tile's 64 fp32 compensations
+  static constexpr int NSD = 6;
+  static constexpr int DRING = BYTES;
+  static constexpr int DBYTES = NSD * 1024;
   static constexpr int KCH = KBYTES / 1024;             // 1 KiB DMA blocks per K tile
   static constexpr int VCH = FP8 ? 0 : VBYTES / 1024;   // (fp16 V)
   __device__ static constexpr int kswz(int r) { return (r / (256 / D)) % (D / 16); }
@@ -168,7 +185,9 @@ struct DmaPlan {
   static_assert(S::KCH % NWH == 0 && S::VCH % NWH == 0, "tile blocks split over a half");
   int koff[KPW];
   int voff[VPW > 0 ? VPW : 1];
+  int doff;  // smooth Q: byte offset of this lane's 4 compensations in a tile (4 copies per 1 KiB)
   __device__ void init(int w, int lane, int64_t kn, int64_t vn) {
+    doff = 16 * (lane & 15);
 #pragma unroll
     for (int x = 0; x < KPW; ++x) {
       const int byte = (w + NWH * x) * 1024 + 16 * lane;
@@ -192,6 +211,9 @@ struct DmaPlan {
   __device__ __forceinline__ void issue_k1(const v4i& kr, lds_u8* slot, int w, int x) const {
     dma_b128(kr, koff[x], lds_addr(slot + (w + NWH * x) * 1024));
   }
+  // smooth Q: the compensations of one tile into a 1 KiB slot (every wave of the
+  // half writes the same bytes)
+  __device__ __forceinline__ void issue_d(const v4i& dr, lds_u8* slot) const { dma_b128(dr, doff, lds_addr(slot)); }
   __device__ __forceinline__ void issue_v1(const v4i& vr, lds_u8* slot, int w, int x) const {
     if constexpr (VPW > 0) dma_b128(vr, voff[x], lds_addr(slot + (w + NWH * x) * 1024));
   }
@@ -284,9 +306,17 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
 __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, lds_u8* const lds) {
   using S = Lds<D, FP8>;
+  static_assert(!SQ || KSU, "smooth Q needs key blocks that are multiples of the tile");
+  // Smooth Q: a zero block scale (all codes 0) is replaced.  x' = x + delta /
+  // (qs ks) is rounded to fp32, so the unit qs ks must not be coarse next to
+  // delta: a zero Q scale becomes 2^-40 (x' then holds delta at fp32 relative
+  // precision); a zero K scale means K_s = 0 in the block, hence delta = 0,
+  // and becomes 1.
+  auto qeff = [](float v) { return (SQ && !(v > 0.0f)) ? 0x1p-40f : v; };
+  auto keff = [](float v) { return (SQ && !(v > 0.0f)) ? 1.0f : v; };
 
   // ---- workgroup -> (sequence, head, query tile).  (sequence, K/V head)
   // groups are dealt round-robin over the 8 XCDs, group = 8 * (slot / grp) +
@@ -322,12 +352,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int row0 = q0 + (w & 3) * 32;
   const int i = row0 + li;
   v4i qf[D / 32];
-  float qsc = 0.0f;
+  float qsc = SQ ? kLog2e : 0.0f;  // (rows past the sequence: never stored; smooth Q keeps them finite)
   if (i < L) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
-    qsc = a.q_scale[sh * p.nbq + i / p.blk_q] * kLog2e;
+    qsc = qeff(a.q_scale[sh * p.nbq + i / p.blk_q]) * kLog2e;
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
@@ -418,7 +448,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // one value per tile, from the LDS table (longer sequences: a scalar
       // load, counted by lgkmcnt rather than by the tile loads' vmcnt)
       const float v = qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
-                                       : ksc_c[min(j0, L - 1) / p.blk_k]);
+                                       : keff(ksc_c[min(j0, L - 1) / p.blk_k]));
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -438,10 +468,24 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 
   // softmax of tile t from sc -> pf / pf8 (lane: row i, keys j(jt, r)).
   // MASKED tiles (sequence tail, causal diagonal) take a separate instantiation.
-  auto softmax = [&](int t, const Ck& ck, auto masked_tag) {
+  auto softmax = [&](int t, const Ck& ck, uint32_t dslot, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = t * BN;
     const auto& c = ck.c;
+    // smooth Q: x' = x + delta_j / (qs ks), in place of the raw scores
+    if constexpr (SQ) {
+      const float f = __builtin_amdgcn_rcpf(c[0][0]) * kLog2e;
+      const lds_u8* dl = lds + dslot + 16 * g;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f d4 = *(const LDS v4f*)(dl + 4 * (32 * jt + 8 * q));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[jt][4 * q + e] = __float_as_int(__builtin_fmaf(d4[e], f, __int_as_float(sc[jt][4 * q + e])));
+        }
+    }
     bool valid[2][16];
     if constexpr (MASKED) {
 #pragma unroll
@@ -456,9 +500,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     float mt;
     float y[2][16];  // general key-block size: S * c per element
     if constexpr (KSU) {
+      // (without smooth Q every real x is > 0, so 0 stands for a masked key)
       auto xv = [&](int jt, int r) {
         const float xx = __int_as_float(sc[jt][r]);
-        if constexpr (MASKED) return valid[jt][r] ? xx : 0.0f;
+        if constexpr (MASKED) return valid[jt][r] ? xx : (SQ ? -INFINITY : 0.0f);
         return xx;
       };
       // four independent max3 chains (one wave does all the VALU work of a
@@ -474,7 +519,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
       mx = xhalf_max(mx);
       // every real x is >= 1.5*2^23 - 2^21 > 0, so 0 means "all masked": leave m alone
-      mt = (MASKED && mx == 0.0f) ? -INFINITY : (mx - kMagic) * c[0][0];
+      // (smooth Q: a masked x is -inf, and so is mt)
+      mt = (MASKED && !SQ && mx == 0.0f) ? -INFINITY : (mx - kMagic) * c[0][0];
     } else {
       float mx = -INFINITY;
 #pragma unroll
@@ -573,7 +619,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // 5); ph = b % 5 is advanced at the end of every phase.
   static_assert(NSK == 5 && NSV == 5, "slot arithmetic below");
   int ph = 0;
+  int pd = 0;  // smooth Q: b % 6, the compensation ring (tile t in slot t % 6)
   auto wrap = [](int x) { return x >= 5 ? x - 5 : x; };
+  auto wrap6 = [](int x) { return x >= 6 ? x - 6 : x; };
+  auto doffs = [](int slot) { return (uint32_t)(S::DRING + slot * 1024); };
   auto koff = [](int slot) { return (uint32_t)(slot * S::KBYTES); };
   auto voff = [](int slot) { return (uint32_t)(S::VRING + slot * S::VBYTES); };
   // Tile loads.  The half that owns tile t (t = hf mod 2) loads K(t) in its
@@ -590,23 +639,28 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // (fp16 V rows hold dv channels: the last row is read up to them only)
   int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
+  // smooth Q: this half's next compensation tile, with K (fp32 per key of this query head)
+  const float* dnext = SQ ? a.q_delta + seq_head_base(p.cu, a.qds, s, h) + hf * BN : nullptr;
+  int drec = (L - hf * BN) * 4;
+  constexpr int dstep = 2 * BN * 4;
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
   constexpr int KL = DmaPlan<D, FP8>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8>::VPW;
-  constexpr int NOPS = KL + VL;  // DMA loads per wave per matrix phase
+  constexpr int NOPS = KL + VL + (SQ ? 1 : 0);  // DMA loads per wave per matrix phase
   // Every matrix phase issues NOPS DMA loads per wave (fp16: VL for V, then KL
-  // for K; FP8: its V loads to registers come first, then the KL K loads).  At
-  // the end of a vector phase the loads of the previous matrix phase may stay
-  // in flight: s_waitcnt vmcnt(NOPS) (FP8: vmcnt(KL), its V registers are
-  // needed now).
+  // for K, then (smooth Q) one for the compensations; FP8: its V loads to
+  // registers come first, then the K and compensation loads).  At the end of a
+  // vector phase the loads of the previous matrix phase may stay in flight:
+  // s_waitcnt vmcnt(NOPS) (FP8: vmcnt(KL (+1)), its V registers are needed now).
   auto wait_older = [&] {
-    constexpr int n = FP8 ? KL : NOPS;
-    static_assert(n >= 1 && n <= 6, "wait counts below");
+    constexpr int n = FP8 ? KL + (SQ ? 1 : 0) : NOPS;
+    static_assert(n >= 1 && n <= 7, "wait counts below");
     if constexpr (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else if constexpr (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     else if constexpr (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else if constexpr (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (n == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   };
 
   // ---- prologue.  LDS starts zeroed, so bytes the tail tiles leave untouched
@@ -622,7 +676,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
       for (int j = 0; j < KSPT; ++j) {
         const int t = tid + j * NT;
-        ksv[j] = t < ntiles ? ksc[(t * BN) / p.blk_k] : 0.0f;
+        ksv[j] = t < ntiles ? keff(ksc[(t * BN) / p.blk_k]) : 0.0f;
       }
     if constexpr (FP8)
       v8s.load(vseq, vn, hf * BN, L, tidh);
@@ -634,6 +688,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     dma.issue_k(make_rsrc(knext + kstep, max(krec - kstep, 0)), lds + koff(hf + 2), wh);
     knext += 2 * kstep;
     krec -= 2 * kstep;
+    if constexpr (SQ) {
+      dma.issue_d(make_rsrc(dnext, max(drec, 0)), lds + doffs(hf));
+      dma.issue_d(make_rsrc(dnext + 2 * BN, max(drec - dstep, 0)), lds + doffs(hf + 2));
+      dnext += 4 * BN;
+      drec -= 2 * dstep;
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
     if (ks_in_lds)
@@ -668,6 +728,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     ph = wrap(ph + 1);
+    if constexpr (SQ) pd = wrap6(pd + 1);
   };
   // Matrix phase with every LDS operand read well ahead of its MFMA: all K
   // fragments and the first V group; then the INT8 MFMAs with this phase's
@@ -743,12 +804,20 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     const v4i vr = make_rsrc(vnext, max(vrec, 0)), kr = make_rsrc(knext, max(krec, 0));
     lds_u8* const vsl = lds + voff(wrap(ph + 2));
     lds_u8* const ksl = lds + koff(wrap(ph + 4));
+    v4i dr{};
+    lds_u8* dsl = nullptr;
+    if constexpr (SQ) {
+      dr = make_rsrc(dnext, max(drec, 0));
+      dsl = lds + doffs(wrap6(pd + 4));  // delta(b+4), with K(b+4)
+    }
     if constexpr (FP8) v8s.load(vseq, vn, (b + 2) * BN, L, tidh);
     auto op = [&](int x) {
       if (x < VL)
         dma.issue_v1(vr, vsl, wh, x);
-      else
+      else if (x < VL + KL)
         dma.issue_k1(kr, ksl, wh, x - VL);
+      else if constexpr (SQ)
+        dma.issue_d(dr, dsl);
     };
     if (FULL) {
       qk_pv(koff(ph), voff(wrap(ph + 3)), op);
@@ -762,20 +831,25 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     krec -= kstep;
     vnext += vstep;
     vrec -= vstep;
+    if constexpr (SQ) {
+      dnext += 2 * BN;
+      drec -= dstep;
+    }
     end_phase(b, false);
   };
   auto vphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int t = b - 1;
     const Ck ck = load_ck(min(max(t, 0), ntiles - 1));  // (t outside the tiles: value unused)
+    const uint32_t dslot = doffs(wrap6(pd + 5));         // tile t = b - 1 (smooth Q)
     if (FULL) {
-      softmax(t, ck, std::false_type{});
+      softmax(t, ck, dslot, std::false_type{});
     } else if (t >= 0 && t < wtiles) {
       const bool masked = (t * BN + BN > L) || (CAUSAL && t * BN + BN - 1 > row0);
       if (masked)
-        softmax(t, ck, std::true_type{});
+        softmax(t, ck, dslot, std::true_type{});
       else
-        softmax(t, ck, std::false_type{});
+        softmax(t, ck, dslot, std::false_type{});
     }
     end_phase(b, true);
   };
@@ -864,10 +938,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   }
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
 __global__ __launch_bounds__(NT) void k_attn(Problem p, AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[Lds<D, FP8>::BYTES];
-  attn_body<D, FP8, CAUSAL, KSU>(p, a, (lds_u8*)lds_raw);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[Lds<D, FP8>::BYTES + (SQ ? Lds<D, FP8>::DBYTES : 0)];
+  attn_body<D, FP8, CAUSAL, KSU, SQ>(p, a, (lds_u8*)lds_raw);
 }
 
 // Debug: the INT32 scores of the same staging (DmaPlan) and MFMA path
@@ -925,20 +999,25 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
   }
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
 hipError_t launch_cfg(const Problem& p, const AttnArgs& a, hipStream_t st) {
   const int nqt = (p.max_seqlen + BM - 1) / BM;
   // slots per XCD: ceil(groups / 8) groups of heads/kv_heads query heads
   const int64_t P8 = ((int64_t)p.nseq * p.kv_heads + 7) / 8 * 8 * (p.heads / p.kv_heads);
   const int64_t G = (int64_t)nqt * P8;
   if (G >= (1ll << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
+  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU, SQ>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
   return hipGetLastError();
 }
 
 template <int D, bool FP8, bool CAUSAL>
 hipError_t launch_ks(const Problem& p, const AttnArgs& a, hipStream_t st) {
-  return (p.blk_k % BN == 0) ? launch_cfg<D, FP8, CAUSAL, true>(p, a, st) : launch_cfg<D, FP8, CAUSAL, false>(p, a, st);
+  if (a.q_delta) {  // smooth Q (key blocks that are multiples of the tile: checked by the caller)
+    if (p.blk_k % BN != 0) return hipErrorInvalidValue;
+    return launch_cfg<D, FP8, CAUSAL, true, true>(p, a, st);
+  }
+  return (p.blk_k % BN == 0) ? launch_cfg<D, FP8, CAUSAL, true, false>(p, a, st)
+                             : launch_cfg<D, FP8, CAUSAL, false, false>(p, a, st);
 }
 
 template <int D>

@@ -7,7 +7,8 @@
 //     item 2: INT8 Q and K with one scale per block of rows (the attention
 //     kernel's tile size).
 //   "4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级", section
-//     技术方案 item 4: V quantised to FP8 E4M3.
+//     技术方案 item 4: V quantised to FP8 E4M3; item 1: smoothing Q (Q minus
+//     its per-channel mean, the mean's product with K^T added to S).
 //
 // All of these are HBM-bound streaming passes.  Rounding is fixed so that the
 // results are bit-exact against a plain CPU implementation:
@@ -211,6 +212,39 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
   return scale;
 }
 
+// Exact fp64 column sums of rows [n0, n1) (n1 - n0 <= kKSumRows) of one
+// (sequence, head): thread (r, cg) adds rows n0 + r + RPP*j of channels 8cg ..
+// 8cg+7 (base points at channel 8cg of token 0), then the RPP partials of a
+// channel are added in LDS and written to out[0 .. D-1].  Every fp16 value is a
+// multiple of 2^-24 and |sum| < 2^29, so the sums are exact in any order.
+template <int D>
+__device__ __forceinline__ void colsum_chunk(const _Float16* __restrict__ base, int64_t sn, int n0, int n1, bool cgv,
+                                             double* __restrict__ out) {
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR;
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  double acc[8] = {};
+  static_assert(kKSumRows <= 128, "a chunk fits the register-cached rows");
+  {
+    BlockRows<D> rows;
+    rows.load(base, sn, n0, n1, cgv);
+#pragma unroll
+    for (int j = 0; j < BlockRows<D>::R; ++j)
+      if (n0 + r + RPP * j < n1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (double)(float)rows.x[j].v[i];
+  }
+  __shared__ double red[RPP][D];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = acc[i];
+  __syncthreads();
+  if (tid < D) {
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < RPP; ++i) t += red[i][tid];
+    out[tid] = t;
+  }
+}
+
 // grid (nqw + nks, heads, nseq), kQThreads (heads: of Q).  Workgroups x < nqw quantise Q
 // (INT8 Q' = Q * sm_scale): block x of blk_q rows, or for blk_q == 1 (one
 // scale per token) the RPP rows x*RPP .. x*RPP+RPP-1, TPR threads per row.
@@ -268,28 +302,31 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
   const int ci = x - nqw;
   const int n0 = ci * kKSumRows;
   if (n0 >= L) return;
+  colsum_chunk<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, min(L, n0 + kKSumRows), cgv,
+                  part + (skv * nks + ci) * D);
+}
+
+// grid (nks, heads, nseq), kQThreads (heads: of Q).  Smooth Q: the fp64 column sums of
+// Q (every query head) and of K (the K heads) over chunk x of kKSumRows tokens.
+template <int D>
+__global__ __launch_bounds__(kQThreads) void k_colsums_qk(const _Float16* __restrict__ Q, Str qs,
+                                                          const _Float16* __restrict__ K, Str ks,
+                                                          const int32_t* __restrict__ cu, int max_seqlen, int nks,
+                                                          int kv_heads, int dv, double* __restrict__ qpart,
+                                                          double* __restrict__ kpart) {
+  const int ci = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = ci * kKSumRows;
+  if (n0 >= L) return;
   const int n1 = min(L, n0 + kKSumRows);
-  const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
-  double acc[8] = {};
-  static_assert(kKSumRows <= 128, "a chunk fits the register-cached rows");
-  {
-    BlockRows<D> krows;
-    krows.load(kb, ks.n, n0, n1, cgv);
-#pragma unroll
-    for (int j = 0; j < BlockRows<D>::R; ++j)
-      if (n0 + r + RPP * j < n1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += (double)(float)krows.x[j].v[i];
-  }
-  __shared__ double red[RPP][D];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[r][cg * 8 + i] = acc[i];
-  __syncthreads();
-  if (tid < D) {
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < RPP; ++i) t += red[i][tid];
-    part[(skv * nks + ci) * D + tid] = t;
+  const int cg = threadIdx.x % (D / 8);
+  const bool cgv = 8 * cg < dv;
+  colsum_chunk<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, cgv,
+                  qpart + (((int64_t)s * H + h) * nks + ci) * D);
+  if (h < kv_heads) {
+    __syncthreads();  // (colsum_chunk's LDS is reused)
+    colsum_chunk<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, n1, cgv,
+                    kpart + (((int64_t)s * kv_heads + h) * nks + ci) * D);
   }
 }
 
@@ -318,17 +355,127 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
   return sum;
 }
 
-// grid (kv heads, nseq), kQThreads: mean = fp32(sum / L) from the
-// partials (long sequences; shorter ones fold this into k_quant_k).
+// grid (heads, nseq), kQThreads: mean = fp32((sum / L) * scale) from the
+// partials (scale 1: K's mean; sm_scale: the mean of Q' = Q * sm_scale); long
+// sequences (shorter ones fold this into the quantisation kernel).
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
                                                              const int32_t* __restrict__ cu, int max_seqlen,
-                                                             int nks, float* __restrict__ km) {
+                                                             int nks, double scale, float* __restrict__ km) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
   const int L = seq_len(cu, s, max_seqlen);
   const int nb = (L + kKSumRows - 1) / kKSumRows;
   const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nks * D + c, nb, c, g);
-  if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)(sum / (double)L) : 0.0f;
+  if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)((sum / (double)L) * scale) : 0.0f;
+}
+
+// grid (nqw, heads, nseq), kQThreads: INT8 Q_s = fp32(fp32(Q * sm_scale) - qm)
+// with qm = mean(Q') (smooth Q), per block of blk_q rows or, blk_q == 1, per
+// token (RPP rows per workgroup).  FOLD: every workgroup sums its head's
+// column partials itself (the first stores q_mean); otherwise q_mean comes
+// from k_mean_finalize.
+template <int D, bool FOLD>
+__global__ __launch_bounds__(kQThreads) void k_quant_q_smooth(const _Float16* __restrict__ Q, Str qs,
+                                                              const int32_t* __restrict__ cu, int max_seqlen,
+                                                              int blk_q, int nbq, int nks, int dv, float sm_scale,
+                                                              const double* __restrict__ qpart,
+                                                              float* __restrict__ qmean, int8_t* __restrict__ q8,
+                                                              Str q8s, float* __restrict__ sq) {
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR;
+  const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const bool cgv = 8 * cg < dv;
+  const int64_t sh = (int64_t)s * H + h;
+  const int n0 = blk_q == 1 ? x * RPP : x * blk_q;
+  if (n0 >= L) return;
+  float mean[8];
+  if constexpr (FOLD) {
+    __shared__ float qm[D];
+    const int c = tid % D, g = tid / D;
+    const double sum = sum_partials<D>(qpart + sh * nks * D + c, (L + kKSumRows - 1) / kKSumRows, c, g);
+    if (g == 0) {
+      const float mv = (float)((sum / (double)L) * (double)sm_scale);
+      qm[c] = mv;
+      if (x == 0) qmean[sh * D + c] = mv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = qm[cg * 8 + i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mean[i] = qmean[sh * D + cg * 8 + i];
+  }
+  // two roundings: the product is not contracted with the subtraction into one
+  // fma (device code contracts by default); monotone non-decreasing in x
+  auto smooth = [&](float v, int i) {
+#pragma clang fp contract(off)
+    return v * sm_scale - mean[i];
+  };
+  if (blk_q == 1) {
+    const int n = n0 + r;
+    const bool valid = n < L;
+    H8 row;
+    float a = 0.0f;
+    if (valid) {
+      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8, cgv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(smooth((float)row.v[i], i)));
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));  // the row's TPR lanes
+    if (valid) {
+      const float scale = a > 0.0f ? a / 127.0f : 0.0f;
+      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h) + (int64_t)n * q8s.n + cg * 8) =
+          a > 0.0f ? codes8(row, smooth, scale, __builtin_amdgcn_rcpf(scale)) : make_uint2(0u, 0u);
+      if (cg == 0) sq[sh * nbq + n] = scale;
+    }
+    return;
+  }
+  const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, min(L, n0 + blk_q), smooth,
+                                     q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n, cgv);
+  if (tid == 0) sq[sh * nbq + x] = scale;
+}
+
+// grid (ceil(max_seqlen / 128), heads, nseq), kQThreads (heads: of Q).  The
+// compensation of smoothing Q for 128 keys of one (sequence, query head):
+// delta_j = sum_c qm_c * fp32(K_jc - km_c), products exact in fp64, added in
+// fp64 (channels in order within a thread, then a butterfly over the row's
+// TPR lanes), rounded once to fp32.
+template <int D>
+__global__ __launch_bounds__(kQThreads) void k_q_delta(const _Float16* __restrict__ K, Str ks,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int kv_heads,
+                                                       int dv, const float* __restrict__ qmean,
+                                                       const float* __restrict__ kmean, float* __restrict__ qdelta,
+                                                       Str qds) {
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
+  const int h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int kvh = h / (H / kv_heads);
+  const int L = seq_len(cu, s, max_seqlen);
+  const int n0 = blockIdx.x * 128;
+  if (n0 >= L) return;
+  const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
+  const bool cgv = 8 * cg < dv;
+  float qm[8], km[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    qm[i] = qmean[((int64_t)s * H + h) * D + cg * 8 + i];
+    km[i] = kmean[((int64_t)s * kv_heads + kvh) * D + cg * 8 + i];
+  }
+  BlockRows<D> rows;
+  rows.load(K + seq_head_base(cu, ks, s, kvh) + cg * 8, ks.n, n0, min(L, n0 + 128), cgv);
+  float* const out = qdelta + seq_head_base(cu, qds, s, h);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int n = n0 + r + RPP * j;
+    double t = 0.0;
+    if (n < L)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t += (double)qm[i] * (double)((float)rows.x[j].v[i] - km[i]);
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) t += __shfl_xor(t, m, 64);
+    if (n < L && cg == 0) out[n] = (float)t;
+  }
 }
 
 // grid (nbk, kv heads, nseq), kQThreads: K block bi -> INT8 K' = K - mean(K).
@@ -587,12 +734,46 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
     return hipGetLastError();
   }
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
-                                                 partial, p.cu, p.max_seqlen, p.nks, k_mean));
+                                                 partial, p.cu, p.max_seqlen, p.nks, 1.0, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
                                                  (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
                                                  p.dv, partial, k_mean, k8, k8s, k_scale));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                                 int8_t* q8, Str q8s, float* q_scale, float* q_mean, double* qpart, double* kpart,
+                                 hipStream_t st) {
+  hipError_t e;
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_colsums_qk<D>), dim3(p.nks, p.heads, p.nseq), dim3(kQThreads), 0,
+                                                 st, (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu,
+                                                 p.max_seqlen, p.nks, p.kv_heads, p.dv, qpart, kpart));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  SAGE_DISPATCH_D(p.head_dim, {
+    constexpr int RPP = kQThreads / (D / 8);
+    const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
+    const dim3 grid(nqw, p.heads, p.nseq);
+    if (p.nks <= kFoldMaxBlocks) {
+      hipLaunchKernelGGL((k_quant_q_smooth<D, true>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
+                         p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
+    } else {
+      hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
+                         p.max_seqlen, p.nks, (double)sm_scale, q_mean);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL((k_quant_q_smooth<D, false>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
+                         p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
+    }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_q_delta(const Problem& p, const void* K, Str ks, const float* q_mean, const float* k_mean,
+                          float* q_delta, Str qds, hipStream_t st) {
+  SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_q_delta<D>), dim3((p.max_seqlen + 127) / 128, p.heads, p.nseq),
+                                                 dim3(kQThreads), 0, st, (const _Float16*)K, ks, p.cu, p.max_seqlen,
+                                                 p.kv_heads, p.dv, q_mean, k_mean, q_delta, qds));
   return hipGetLastError();
 }
 

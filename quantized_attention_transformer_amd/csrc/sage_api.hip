@@ -57,6 +57,16 @@ int check_problem(const sage_problem* p, bool allow_d96 = false) {
   if (p->kv_heads < 0 || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
     return fail(SAGE_ERR_INVALID_ARG, "kv_heads (%d) must divide heads (%d) (0: same as heads)", p->kv_heads,
                 p->heads);
+  if (p->smooth_q != 0 && p->smooth_q != 1) return fail(SAGE_ERR_INVALID_ARG, "smooth_q must be 0 or 1");
+  if (p->smooth_q && p->blk_k % 64 != 0)
+    return fail(SAGE_ERR_UNSUPPORTED, "smooth_q needs blk_k to be a multiple of 64 (got %d)", p->blk_k);
+  return SAGE_OK;
+}
+
+// Entries that take caller-laid-out int8 Q without the smooth-Q compensation.
+int no_smooth_q(const sage_problem* p, const char* name) {
+  if (p->smooth_q)
+    return fail(SAGE_ERR_UNSUPPORTED, "%s does not take smooth_q (use sage_quantize_smooth_q / sage_attn)", name);
   return SAGE_OK;
 }
 
@@ -77,6 +87,7 @@ sage::Problem to_internal(const sage_problem* p) {
   q.nbk = (int)cdiv(p->max_seqlen, p->blk_k);
   q.nchunk = (int)cdiv(p->max_seqlen, sage::kColChunk);
   q.nks = (int)cdiv(p->max_seqlen, sage::kKSumRows);
+  q.smooth_q = p->smooth_q;
   return q;
 }
 
@@ -111,9 +122,20 @@ int kv_heads_of(const sage_problem* p) { return p->kv_heads > 0 ? p->kv_heads : 
 // are stored head-major: dense [nseq][heads][max_seqlen][d], packed
 // [heads][total_tokens][d] (K and V with kv_heads heads).
 struct WsLayout {
-  size_t q8, k8, sq, sk, km, colsum, v8, sv, vpsum, vpmax, vpmin, total;
-  sage_strides s8q, s8kv;
+  size_t q8, k8, sq, sk, km, colsum, v8, sv, vpsum, vpmax, vpmin, qpart, qm, qdelta, total;
+  sage_strides s8q, s8kv, sqd;
 };
+
+// Strides of q_delta (one fp32 per (sequence, query head, token)): dense
+// [nseq][heads][max_seqlen], packed [heads][total_tokens].
+sage_strides qdelta_strides(const sage_problem* p) {
+  const int64_t T = p->cu_seqlens ? p->total_tokens : (int64_t)p->max_seqlen;
+  return p->cu_seqlens ? sage_strides{0, T, 1} : sage_strides{(int64_t)p->heads * T, T, 1};
+}
+int64_t tokens(const sage_problem* p);
+size_t qdelta_count(const sage_problem* p) {
+  return (size_t)(p->cu_seqlens ? tokens(p) : (int64_t)p->nseq * p->max_seqlen) * p->heads;
+}
 
 bool valid_pv_mode(int m) { return m == SAGE_PV_FP16 || m == SAGE_PV_FP8 || m == SAGE_PV_FP8_SMOOTH_V; }
 
@@ -162,6 +184,12 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
     w.vpmin = v.pmin;
     off += v.total;
   }
+  if (p->smooth_q) {
+    w.qpart = take((size_t)p->nseq * H * q.nks * d * 8);
+    w.qm = take((size_t)p->nseq * H * d * 4);
+    w.qdelta = take(qdelta_count(p) * 4);
+  }
+  w.sqd = qdelta_strides(p);
   w.total = off;
   if (p->cu_seqlens) {
     w.s8q = sage_strides{0, T * d, d};
@@ -176,6 +204,29 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
 size_t quantize_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
   return align_up((size_t)p->nseq * q.kv_heads * q.nks * q.head_dim * 8);
+}
+
+// sage_quantize_smooth_q: K column-sum partials, then Q's.
+size_t quantize_sq_ws_bytes(const sage_problem* p) {
+  const sage::Problem q = to_internal(p);
+  return quantize_ws_bytes(p) + align_up((size_t)p->nseq * p->heads * q.nks * q.head_dim * 8);
+}
+
+int run_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                          float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
+                          float* k_scale, float* k_mean, float* q_mean, float* q_delta, sage_strides qds,
+                          double* kpart, double* qpart, hipStream_t st) {
+  const sage::Problem q = to_internal(p);
+  if (sm_scale <= 0.0f || !std::isfinite(sm_scale)) sm_scale = (float)(1.0 / std::sqrt((double)p->head_dim));
+  hipError_t e;
+  if ((e = sage::launch_quant_q_smooth(q, Q, S(qs), K, S(ks), sm_scale, q8, S(q8s), q_scale, q_mean, qpart, kpart,
+                                       st)) != hipSuccess)
+    return hip_fail(e, "smooth-Q quantisation launch");
+  if ((e = sage::launch_quant_k(q, K, S(ks), kpart, k_mean, k8, S(k8s), k_scale, st)) != hipSuccess)
+    return hip_fail(e, "quant_k launch");
+  if ((e = sage::launch_q_delta(q, K, S(ks), q_mean, k_mean, q_delta, S(qds), st)) != hipSuccess)
+    return hip_fail(e, "q_delta launch");
+  return SAGE_OK;
 }
 
 int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
@@ -244,7 +295,7 @@ int sage_quantize(const sage_problem* p, const void* Q, sage_strides qs, const v
                   float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
                   float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
-  if (rc) return rc;
+  if (rc || (rc = no_smooth_q(p, "sage_quantize"))) return rc;
   if (empty(p)) return SAGE_OK;
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
       (rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)))
@@ -255,6 +306,37 @@ int sage_quantize(const sage_problem* p, const void* Q, sage_strides qs, const v
   if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   return run_quantize(p, Q, qs, K, ks, sm_scale, q8, q8s, k8, k8s, q_scale, k_scale, k_mean, (double*)workspace,
                       (hipStream_t)stream);
+}
+
+int sage_quantize_smooth_q_workspace_bytes(const sage_problem* p, size_t* bytes) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = quantize_sq_ws_bytes(p);
+  return SAGE_OK;
+}
+
+int sage_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                           float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
+                           float* k_scale, float* k_mean, float* q_mean, float* q_delta, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!p->smooth_q) return fail(SAGE_ERR_INVALID_ARG, "sage_quantize_smooth_q needs p->smooth_q = 1");
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
+      (rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)))
+    return rc;
+  if (!q_scale || !k_scale || !k_mean || !q_mean || !q_delta)
+    return fail(SAGE_ERR_INVALID_ARG, "scale/mean/delta outputs must not be NULL");
+  const size_t need = quantize_sq_ws_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  return run_quantize_smooth_q(p, Q, qs, K, ks, sm_scale, q8, q8s, k8, k8s, q_scale, k_scale, k_mean, q_mean, q_delta,
+                               qdelta_strides(p), (double*)ws, (double*)(ws + quantize_ws_bytes(p)),
+                               (hipStream_t)stream);
 }
 
 int sage_quantize_v_fp8_smooth_workspace_bytes(const sage_problem* p, size_t* bytes) {
@@ -293,7 +375,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
                         sage_strides k8s, const float* q_scale, const float* k_scale, const void* V, sage_strides vs,
                         const float* v_scale, void* out, sage_strides os, int causal, int pv_mode, void* stream) {
   int rc = check_problem(p);
-  if (rc) return rc;
+  if (rc || (rc = no_smooth_q(p, "sage_attn_quantized"))) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
   const bool fp8 = pv_mode != SAGE_PV_FP16;
@@ -304,7 +386,8 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
   if ((rc = check_row_span("k8", k8s, 1, p)) || (rc = check_row_span("V", vs, fp8 ? 1 : 2, p))) return rc;
   const float* v_mean =
       pv_mode == SAGE_PV_FP8_SMOOTH_V ? v_scale + (size_t)p->nseq * kv_heads_of(p) * p->head_dim : nullptr;
-  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr, v_mean};
+  sage::AttnArgs a{q8, S(q8s), k8, S(k8s), q_scale, k_scale, V, S(vs), v_scale, out, S(os), nullptr, v_mean, nullptr,
+                   sage::Str{0, 0, 0}};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, fp8, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;
@@ -331,9 +414,15 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   int8_t* k8 = (int8_t*)(ws + w.k8);
   float* sq = (float*)(ws + w.sq);
   float* sk = (float*)(ws + w.sk);
-  if ((rc = run_quantize(p, Q, qs, K, ks, sm_scale, q8, w.s8q, k8, w.s8kv, sq, sk, (float*)(ws + w.km),
-                         (double*)(ws + w.colsum), st)))
+  if (p->smooth_q) {
+    if ((rc = run_quantize_smooth_q(p, Q, qs, K, ks, sm_scale, q8, w.s8q, k8, w.s8kv, sq, sk, (float*)(ws + w.km),
+                                    (float*)(ws + w.qm), (float*)(ws + w.qdelta), w.sqd, (double*)(ws + w.colsum),
+                                    (double*)(ws + w.qpart), st)))
+      return rc;
+  } else if ((rc = run_quantize(p, Q, qs, K, ks, sm_scale, q8, w.s8q, k8, w.s8kv, sq, sk, (float*)(ws + w.km),
+                                (double*)(ws + w.colsum), st))) {
     return rc;
+  }
   const void* vin = V;
   sage_strides vin_s = vs;
   const float* sv = nullptr;
@@ -352,7 +441,8 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
     vin_s = w.s8kv;
     sv = (const float*)(ws + w.sv);
   }
-  sage::AttnArgs a{q8, S(w.s8q), k8, S(w.s8kv), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean};
+  sage::AttnArgs a{q8, S(w.s8q), k8, S(w.s8kv), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean,
+                   p->smooth_q ? (const float*)(ws + w.qdelta) : nullptr, S(w.sqd)};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode != SAGE_PV_FP16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;

@@ -35,6 +35,7 @@ struct Problem {
                          // (head dimension 96 runs on the 128-channel kernels, channels 96..127 zero)
   int nbq, nbk, nchunk;  // ceil(max_seqlen/blk_q), ceil(max_seqlen/blk_k), ceil(max_seqlen/kColChunk)
   int nks;               // ceil(max_seqlen/kKSumRows): K column-sum partials per (sequence, head)
+  int smooth_q;          // Q smoothed by its mean; S compensated by q_delta (key blocks: multiples of 64)
 };
 
 // ---- pre-pass (prepass.hip) ----
@@ -45,6 +46,16 @@ hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const 
 // k_mean = fp32(sum of the partials / L) per (sequence, head, channel), and INT8 K blocks of K - k_mean.
 hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
                           Str k8s, float* k_scale, hipStream_t st);
+// Smooth Q: fp64 column sums of Q (qpart: nseq*heads*nks*head_dim) and of K (kpart, as
+// launch_quant_q_colsum's partial), q_mean = fp32((sum / L) * sm_scale) per (sequence, query
+// head, channel), and INT8 blocks of Q_s = fp32(fp32(Q * sm_scale) - q_mean).
+hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                                 int8_t* q8, Str q8s, float* q_scale, float* q_mean, double* qpart, double* kpart,
+                                 hipStream_t st);
+// q_delta[s, h, n] = q_mean[s, h] . fp32(K[s, kvh(h), n] - k_mean[s, kvh(h)]) (fp64 sum, fp32 result);
+// element (s, h, n) at seq_head_base(cu, qds, s, h) + n.
+hipError_t launch_q_delta(const Problem& p, const void* K, Str ks, const float* q_mean, const float* k_mean,
+                          float* q_delta, Str qds, hipStream_t st);
 // v_scale = max|V| / 448 per (sequence, head, channel): zero fill, atomic column max, divide in place.
 hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* v_scale, hipStream_t st);
 hipError_t launch_v_scale(const Problem& p, float* v_scale, hipStream_t st);
@@ -72,6 +83,8 @@ struct AttnArgs {
   Str os;
   int32_t* dump;  // debug i32 scores or nullptr
   const float* v_mean;  // FP8 with smoothed V: per-channel mean added to O, else nullptr
+  const float* q_delta;  // smooth Q: per (sequence, query head, key) compensation added to S, else nullptr
+  Str qds;               // its strides (n = 1)
 };
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
 // One FP8 P.V MFMA on given operands (debug; one wave).

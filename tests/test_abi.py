@@ -77,6 +77,8 @@ def test_workspace_bytes_layout():
     (dict(blk_q=2), -1),
     (dict(kv_heads=3), -1),
     (dict(kv_heads=-1), -1),
+    (dict(smooth_q=2), -1),
+    (dict(smooth_q=1, blk_k=16), -2),
     (dict(blk_k=512), -1),
     (dict(blk_k=0), -1),
     (dict(heads=0), -1),
@@ -215,3 +217,33 @@ def test_binding_requires_max_seqlen_for_varlen():
     cu = torch.tensor([0, 10], dtype=torch.int32)
     with pytest.raises(ValueError):
         sage.make_problem(q, cu_seqlens=cu)
+
+
+def test_smooth_q_workspace_and_entry_rules():
+    rc, n = _ws(_prob())
+    rcs, ns = _ws(_prob(smooth_q=1))
+    # plus Q's column-sum partials (2 heads x 2 chunks x 64 channels x 8 bytes), mean(Q')
+    # (2 x 64 floats) and the per-key compensation (2 heads x 256 tokens x 4 bytes)
+    assert rc == 0 and rcs == 0 and ns == n + 2048 + 512 + 2048
+    m = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_smooth_q_workspace_bytes(ctypes.byref(_prob(smooth_q=1)), ctypes.byref(m)) == 0
+    assert m.value == 2048 + 2048
+    st = _strides()
+    # sage_quantize and sage_attn_quantized do not take smooth_q; sage_quantize_smooth_q needs it
+    p = _prob(smooth_q=1)
+    r = sage.lib().sage_quantize(ctypes.byref(p), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE, FAKE,
+                                 FAKE, 1 << 20, None)
+    assert r == -2 and "smooth_q" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_attn_quantized(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, FAKE, FAKE, st, FAKE, FAKE, st,
+                                       0, 0, None)
+    assert r == -2
+    p0 = _prob()
+    r = sage.lib().sage_quantize_smooth_q(ctypes.byref(p0), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert r == -1
+    r = sage.lib().sage_quantize_smooth_q(ctypes.byref(p), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE,
+                                          FAKE, FAKE, None, FAKE, 1 << 20, None)
+    assert r == -1 and "delta" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_quantize_smooth_q(ctypes.byref(p), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, m.value - 1, None)
+    assert r == -3
