@@ -13,10 +13,10 @@ on the stream it runs on.  cpu_baseline = the CPU oracle on the same step.
 timing = median and min of the per-launch HIP event times (fused kernel,
 non-causal and causal), the sage_quantize pre-pass against the HBM peak
 (algorithmic bytes: fp16 Q and K read once, int8 written, scales, mean), and
-sage_attn end to end (its own workspace); sclk_mhz = amd-smi's shader clock
-sampled while the kernel runs back to back.  inputs_sha256 = provenance of
+sage_attn end to end (its own workspace).  inputs_sha256 = provenance of
 the synthetic fp16 Q, K, V.
-extra = kernel-only TOPS of the fused kernel on the larger workloads.
+extra = kernel-only TOPS of the fused kernel on the larger workloads, and
+sage_attn end to end (pre-pass included) plain and with Q smoothed on one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -211,7 +211,6 @@ def main():
 
     if not args.no_extra:
         result["extra"] = extra_workloads(sage, torch, dev)
-        result["timing"]["sclk_mhz"] = sample_sclk(lambda: attention(False), torch)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, wl, ops_nc + ops_c)
@@ -245,33 +244,6 @@ def end_to_end(sage, torch, q, k, v, wl, ops_nc, ops_c, warmup=10, runs=50):
     return res
 
 
-def sample_sclk(run, torch, max_s=8.0):
-    """Shader clock while the fused kernel runs back to back: `amd-smi metric -c`
-    sampled once under load (mean and range over the XCDs), or the error."""
-    import subprocess
-    try:
-        proc = subprocess.Popen(["amd-smi", "metric", "-c", "--json"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except OSError as e:
-        return {"error": str(e)}
-    t0 = time.time()
-    while proc.poll() is None and time.time() - t0 < max_s:
-        for _ in range(200):
-            run()
-        torch.cuda.synchronize()
-    try:
-        txt, _ = proc.communicate(timeout=10)
-        data = json.loads(txt)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clks = [v["clk"]["value"] for kk, v in gpu["clock"].items() if kk.startswith("gfx") and isinstance(v, dict)]
-        clks = [float(c) for c in clks if isinstance(c, (int, float))]
-        return {"mean": round(sum(clks) / len(clks), 1), "min": min(clks), "max": max(clks), "xcds": len(clks),
-                "source": "amd-smi metric -c, sampled once while the non-causal kernel ran back to back"}
-    except Exception as e:  # noqa: BLE001  (report, never fail the bench over the clock reading)
-        proc.kill()
-        return {"error": f"{type(e).__name__}: {e}"}
-
-
 def extra_workloads(sage, torch, dev):
     """Kernel-only TOPS of the fused attention on the larger workloads
     (inputs drawn on the GPU with the workloads' distributions)."""
@@ -284,7 +256,10 @@ def extra_workloads(sage, torch, dev):
              ("fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, None),
              ("video B2 H24 N16384 d64", synth.VIDEO, False, 0, None),
              ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen"),
-             ("gqa causal B1 H32 kv8 N8192 d128", synth.LONG, True, 0, "gqa")]
+             ("gqa causal B1 H32 kv8 N8192 d128", synth.LONG, True, 0, "gqa"),
+             # whole forward pass (sage_attn: pre-pass + fused kernel), plain and with Q smoothed
+             ("sage_attn fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "e2e"),
+             ("sage_attn smooth-Q fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "sq")]
     for name, wl, causal, mode, kind in cases:
         g.manual_seed(wl.seed)
         if kind == "varlen":
@@ -313,8 +288,17 @@ def extra_workloads(sage, torch, dev):
         qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
         vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
         out = torch.empty_like(q)
+        ws = None
+        if kind in ("e2e", "sq"):
+            prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k)
+            prob.smooth_q = int(kind == "sq")
+            ws = torch.empty(sage.workspace_bytes(prob, mode), dtype=torch.uint8, device=dev)
 
         def run():
+            if ws is not None:
+                sage.attn(q, k, v, causal=causal, pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out,
+                          workspace=ws, smooth_q=(kind == "sq"))
+                return
             sage.attn_quantized(qd["q8"], qd["k8"], qd["q_scale"], qd["k_scale"], vv, v_scale=sv, causal=causal,
                                 pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out, **kw)
         for _ in range(2):
@@ -331,7 +315,7 @@ def extra_workloads(sage, torch, dev):
         ops = sage.attention_ops(seqlens, wl.heads, wl.head_dim, causal)
         tops = ops / (ms * 1e-3) / 1e12
         res[name] = {"kernel_ms": round(ms, 4), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-        del q, k, v, qd, vv, out
+        del q, k, v, qd, vv, out, ws
         torch.cuda.empty_cache()
     return res
 
