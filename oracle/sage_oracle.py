@@ -60,6 +60,15 @@ of Q'; the product of mean(Q') with K_s^T, one value per key (delta_j =
 mean(Q') . K_s[j] in fp64), is added to every row of S in step 6, which
 makes S equal to Q' K_s^T again up to quantisation.
 
+4-bit Q and K ([SA2] 技术方案, its INT4 kernel): gfx950 has no INT4 matrix
+instruction; its 4-bit one takes OCP MXFP4, so the 4-bit variant here
+quantises Q' (or Q_s) and the smoothed K to MXFP4 instead: per row, per block
+of 32 channels, one power-of-two scale 2^e with e = floor(log2(max|x|)) - 2
+(E2M1's largest power of two is 2^2; E8M0 code e + 127, clamped to [-127,
+127]; an all-zero block gets code 0), and elements E2M1(x / 2^e), round to
+nearest even, saturating at 6.  S is then exact from the codes: sum over the
+blocks of 2^(eq + ek) times the E2M1 dot product (mx_* functions).
+
 K and V may have fewer heads than Q (grouped-query attention, which the
 scaled-dot-product-attention interface the pages' drop-in replaces accepts):
 query head h reads K/V head h // (Hq / Hk), and K's mean is per K head.
@@ -322,6 +331,124 @@ def quant_v_fp8(v: np.ndarray, seqlens, cu, smooth: bool = False):
 
 
 # --------------------------------------------------------------------------
+# 4-bit Q and K: OCP MXFP4 (E2M1 elements, one E8M0 scale per 32 channels of a row)
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def e2m1_value(code: int) -> float:
+    """Value of an E2M1 code (bit 3 sign, bits 2-1 exponent with bias 1, bit 0
+    mantissa; exponent 0 is subnormal: 0 or 0.5).  Magnitudes: 0, 0.5, 1, 1.5,
+    2, 3, 4, 6."""
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    mag = m * 0.5 if e == 0 else (1.0 + 0.5 * m) * 2.0 ** (e - 1)
+    return sign * mag
+
+
+_E2M1_POS = np.array([e2m1_value(c) for c in range(8)], np.float64)   # codes 0..7, increasing
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    table = np.array([e2m1_value(c) for c in range(16)], np.float64)
+    return table[np.asarray(codes, np.uint8) & 0xF]
+
+
+def e2m1_encode(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E2M1 value, ties to the even code, saturating at 6;
+    the sign bit is the input's (so negative values that round to 0 give 0x8)."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    lo = np.clip(np.searchsorted(_E2M1_POS, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    dlo = a - _E2M1_POS[lo]
+    dhi = _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi != lo) & (hi % 2 == 0))
+    code = np.where(a >= 6.0, 7, np.where(pick_hi, hi, lo))
+    return (code | np.where(np.signbit(x), 0x8, 0)).astype(np.uint8)
+
+
+def mx_scale_code(amax: float) -> int:
+    """E8M0 code of a block whose largest magnitude is amax: 127 + floor(log2
+    amax) - 2, clamped to [0, 254]; 0 for an all-zero block."""
+    if amax == 0:
+        return 0
+    k = math.frexp(float(amax))[1] - 1          # floor(log2 amax), exact
+    return int(min(254, max(0, 127 + k - 2)))
+
+
+def mx_quant_rows(x: np.ndarray):
+    """MXFP4 of every row of x (fp32 [L, d], d a multiple of 32): returns
+    (E2M1 codes uint8 [L, d], one per element; E8M0 scale codes uint8
+    [L, d/32])."""
+    L, d = x.shape
+    xb = np.asarray(x, np.float64).reshape(L, d // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    sc = np.array([[mx_scale_code(a) for a in row] for row in amax], np.uint8).reshape(L, d // MX_BLOCK)
+    codes = e2m1_encode(xb / np.exp2(sc.astype(np.float64) - 127.0)[:, :, None])
+    codes[np.broadcast_to((amax == 0)[:, :, None], codes.shape)] = 0
+    return codes.reshape(L, d), sc
+
+
+def mx_dequant(codes: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    """Values of MXFP4 rows (fp64 [L, d])."""
+    L, d = codes.shape
+    v = e2m1_decode(codes).reshape(L, d // MX_BLOCK, MX_BLOCK)
+    return (v * np.exp2(sc.astype(np.float64) - 127.0)[:, :, None]).reshape(L, d)
+
+
+def quantize_qk_fp4(q: np.ndarray, k: np.ndarray, seqlens: Sequence[int], cu: Optional[np.ndarray],
+                    sm_scale=None, smooth_q: bool = False):
+    """The 4-bit variant of quantize_qk: Q' (or, smooth_q, Q_s) and the smoothed
+    K quantised to MXFP4.  Returns q4, k4 (E2M1 codes, one per element, in the
+    inputs' layouts), qsc [nseq, Hq, maxL, d/32] and ksc [nseq, Hk, maxL, d/32]
+    (E8M0 codes, 0 past a sequence's end), km, and with smooth_q qm and qdelta
+    as in quantize_qk."""
+    nseq = len(seqlens)
+    H, d = q.shape[-2], q.shape[-1]
+    Hk = k.shape[-2]
+    grp = H // Hk
+    maxL = int(max(seqlens)) if nseq else 0
+    sm = default_sm_scale(d) if sm_scale is None else np.float32(sm_scale)
+    q4 = np.zeros(q.shape, np.uint8)
+    k4 = np.zeros(k.shape, np.uint8)
+    qsc = np.zeros((nseq, H, maxL, d // MX_BLOCK), np.uint8)
+    ksc = np.zeros((nseq, Hk, maxL, d // MX_BLOCK), np.uint8)
+    km = np.zeros((nseq, Hk, d), np.float32)
+    qm = np.zeros((nseq, H, d), np.float32)
+    qdel = np.zeros((nseq, H, maxL), np.float64)
+    qv, kv = _seq_views(q, cu, nseq), _seq_views(k, cu, nseq)
+    q4v, k4v = _seq_views(q4, cu, nseq), _seq_views(k4, cu, nseq)
+    for s in range(nseq):
+        L = int(seqlens[s])
+        k_s = []
+        for h in range(Hk):
+            km[s, h] = k_mean(kv[s][:L, h, :])
+            ks = smooth_k(kv[s][:L, h, :], km[s, h])
+            k_s.append(ks)
+            k4v[s][:L, h, :], ksc[s, h, :L] = mx_quant_rows(ks)
+        for h in range(H):
+            qf = fold_sm_scale(qv[s][:L, h, :], sm)
+            if smooth_q:
+                qm[s, h] = q_mean(qv[s][:L, h, :], sm)
+                qf = smooth_q_values(qf, qm[s, h])
+                qdel[s, h, :L] = q_delta(qm[s, h], k_s[h // grp])
+            q4v[s][:L, h, :], qsc[s, h, :L] = mx_quant_rows(qf)
+    out = dict(q4=q4, k4=k4, qsc=qsc, ksc=ksc, km=km, sm_scale=sm)
+    if smooth_q:
+        out.update(qm=qm, qdelta=qdel)
+    return out
+
+
+def scores_fp4(q4h, qsch, k4h, ksch) -> np.ndarray:
+    """S = (MXFP4 Q) (MXFP4 K)^T in fp64 for one (sequence, head): every product
+    of two E2M1 values times two powers of two is exact."""
+    return mx_dequant(q4h, qsch) @ mx_dequant(k4h, ksch).T
+
+
+# --------------------------------------------------------------------------
 # steps 6-8: dequantise, mask, softmax, P.V
 # --------------------------------------------------------------------------
 
@@ -341,21 +468,26 @@ def fp8_probs(S):
 
 
 def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
-                   pv_fp8=False, v8h=None, svh=None, return_lse=False, vmh=None, qdel=None):
+                   pv_fp8=False, v8h=None, svh=None, return_lse=False, vmh=None, qdel=None, fp4=None):
     """One (sequence, head).  q8h, k8h: int8 [L, d]; sqh, skh: per-block scales;
     vh: fp16 [L, d]; rows: query indices to compute (default all); FP8 path:
     v8h, svh and, with smooth V, vmh (the mean added back to O: every row of
     P sums to 1, so P V = P (V - mean) + mean); smooth Q: qdel [L], the
-    per-key compensation mean(Q') . K_s^T added to every row of S.
+    per-key compensation mean(Q') . K_s^T added to every row of S; 4-bit Q and
+    K: fp4 = (q4h, qsch, k4h, ksch) in place of q8h ... skh (S from scores_fp4).
     Returns O fp64 [len(rows), d]."""
-    L = q8h.shape[0]
+    L = vh.shape[0]
     rows = np.arange(L) if rows is None else np.asarray(rows)
     if len(rows) == 0 or L == 0:
         return np.zeros((len(rows), vh.shape[1]), np.float64)
-    s_int = scores_int(q8h[rows], k8h)                               # step 5
-    rs = sqh[rows // blk_q].astype(np.float64)
-    cs = skh[np.arange(L) // blk_k].astype(np.float64)
-    S = s_int.astype(np.float64) * rs[:, None] * cs[None, :]         # step 6
+    if fp4 is not None:
+        q4h, qsch, k4h, ksch = fp4
+        S = scores_fp4(q4h[rows], qsch[rows], k4h, ksch)
+    else:
+        s_int = scores_int(q8h[rows], k8h)                           # step 5
+        rs = sqh[rows // blk_q].astype(np.float64)
+        cs = skh[np.arange(L) // blk_k].astype(np.float64)
+        S = s_int.astype(np.float64) * rs[:, None] * cs[None, :]     # step 6
     if qdel is not None:
         S = S + np.asarray(qdel, np.float64)[None, :L]
     if causal:
@@ -378,23 +510,30 @@ def attention_head(q8h, k8h, sqh, skh, vh, blk_q, blk_k, causal, rows=None,
 
 
 def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=False,
-              rows_by_seq=None, smooth=True, quant=None, smooth_v=False, smooth_q=False):
+              rows_by_seq=None, smooth=True, quant=None, smooth_v=False, smooth_q=False, qk_fp4=False):
     """The whole forward pass.  Layouts as in quantize_qk.  rows_by_seq
     optionally maps a sequence index to the query rows to compute (the rest
     of O is left NaN).  smooth_v (FP8 path): subtract mean(V) before the E4M3
     quantisation and add it to O.  smooth_q: smooth Q as well (quantize_qk).
+    qk_fp4: 4-bit (MXFP4) Q and K (quantize_qk_fp4; blk_q and blk_k unused).
     Returns (O fp64 in Q's layout, quantisation dict)."""
     nseq = len(seqlens)
     H = q.shape[-2]
     grp = H // k.shape[-2]  # query heads per K/V head (grouped-query attention)
-    qd = quant if quant is not None else quantize_qk(q, k, seqlens, cu, blk_q, blk_k, sm_scale,
-                                                     smooth=smooth, smooth_q=smooth_q)
+    if quant is not None:
+        qd = quant
+    elif qk_fp4:
+        qd = quantize_qk_fp4(q, k, seqlens, cu, sm_scale, smooth_q=smooth_q)
+    else:
+        qd = quantize_qk(q, k, seqlens, cu, blk_q, blk_k, sm_scale, smooth=smooth, smooth_q=smooth_q)
     if pv_fp8:
         v8, sv, vm = quant_v_fp8(v, seqlens, cu, smooth_v)
         qd = dict(qd, v8=v8, sv=sv, vm=vm)
     O = np.full(q.shape, np.nan, np.float64)
     ov = _seq_views(O, cu, nseq)
-    q8v, k8v, vv = (_seq_views(a, cu, nseq) for a in (qd["q8"], qd["k8"], v))
+    fp4 = "q4" in qd
+    q8v, k8v = (_seq_views(qd[a], cu, nseq) for a in (("q4", "k4") if fp4 else ("q8", "k8")))
+    vv = _seq_views(v, cu, nseq)
     v8v = _seq_views(qd["v8"], cu, nseq) if pv_fp8 else None
     for s in range(nseq):
         L = int(seqlens[s])
@@ -403,8 +542,10 @@ def sage_attn(q, k, v, seqlens, cu, causal, blk_q, blk_k, sm_scale=None, pv_fp8=
             continue
         for h in range(H):
             kh = h // grp
-            o = attention_head(q8v[s][:L, h], k8v[s][:L, kh], qd["sq"][s, h], qd["sk"][s, kh],
-                               vv[s][:L, kh], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8,
+            f4 = (q8v[s][:L, h], qd["qsc"][s, h, :L], k8v[s][:L, kh], qd["ksc"][s, kh, :L]) if fp4 else None
+            o = attention_head(None if fp4 else q8v[s][:L, h], None if fp4 else k8v[s][:L, kh],
+                               None if fp4 else qd["sq"][s, h], None if fp4 else qd["sk"][s, kh],
+                               vv[s][:L, kh], blk_q, blk_k, causal, rows=rows, pv_fp8=pv_fp8, fp4=f4,
                                v8h=None if v8v is None else v8v[s][:L, kh],
                                svh=None if v8v is None else qd["sv"][s, kh],
                                vmh=qd["vm"][s, kh] if (pv_fp8 and smooth_v) else None,

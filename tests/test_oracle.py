@@ -591,3 +591,116 @@ def test_smooth_q_gqa_equals_repeated_kv_heads(hk):
         om, qm = O.sage_attn(q, rep(k), rep(v), [L], None, causal, 32, 64, smooth_q=True)
         np.testing.assert_array_equal(og, om)
         np.testing.assert_array_equal(qg["qdelta"], qm["qdelta"])
+
+
+# ---------------------------------------------------------------- 4-bit Q and K (MXFP4)
+
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def exact_e2m1(x: Fraction) -> int:
+    """Nearest E2M1 code to x, ties to the even code, saturating at 6; sign bit of x."""
+    mags = [Fraction(v) for v in E2M1_TABLE[:8]]
+    a = abs(x)
+    if a >= 6:
+        c = 7
+    else:
+        best = min(range(8), key=lambda i: (abs(mags[i] - a), i % 2))
+        c = best
+    return c | (8 if x < 0 else 0)
+
+
+def test_e2m1_table():
+    for code, want in enumerate(E2M1_TABLE):
+        got = O.e2m1_value(code)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want)
+    # every value encodes to its own code; midpoints go to the even neighbour
+    for code in range(16):
+        if code == 8:
+            continue
+        assert int(O.e2m1_encode(np.array([E2M1_TABLE[code]]))[0]) == code
+    mids = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6, 6.5: 7, 100.0: 7}
+    for x, c in mids.items():
+        assert int(O.e2m1_encode(np.array([x]))[0]) == c
+        assert int(O.e2m1_encode(np.array([-x]))[0]) == c | 8
+
+
+def test_ex_i_mxfp4():
+    g = GOLD["ex_i_mxfp4"]
+    row = np.array([g["row"]], np.float32)
+    codes, sc = O.mx_quant_rows(row)
+    assert [int(x) for x in sc[0]] == g["scale_codes"]
+    assert [int(x) for x in codes[0]] == g["codes"]
+    # exact re-derivation from the definition (rationals)
+    for b in range(4):
+        blk = [Fraction(float(x)) for x in row[0, 32 * b:32 * b + 32]]
+        amax = max(abs(x) for x in blk)
+        if amax == 0:
+            assert sc[0, b] == 0 and not codes[0, 32 * b:32 * b + 32].any()
+            continue
+        k = math.floor(math.log2(amax))
+        while Fraction(2) ** k > amax:
+            k -= 1
+        while Fraction(2) ** (k + 1) <= amax:
+            k += 1
+        assert sc[0, b] == 127 + k - 2
+        scale = Fraction(2) ** (k - 2)
+        assert [exact_e2m1(x / scale) for x in blk] == [int(c) for c in codes[0, 32 * b:32 * b + 32]]
+
+
+def test_fp4_scores_brute_force_in_rationals():
+    rng = np.random.default_rng(61)
+    L, d = 5, 64
+    x = (rng.standard_normal((L, d)) * np.exp2(rng.integers(-6, 6, size=(L, 1)))).astype(np.float32)
+    y = (rng.standard_normal((L + 2, d)) * np.exp2(rng.integers(-6, 6, size=(L + 2, 1)))).astype(np.float32)
+    x[:, 32:] *= 37.0  # the two blocks of a row get different scales
+    qc, qs = O.mx_quant_rows(x)
+    kc, ks = O.mx_quant_rows(y)
+    S = O.scores_fp4(qc, qs, kc, ks)
+    for i in range(L):
+        for j in range(L + 2):
+            tot = Fraction(0)
+            for c in range(d):
+                b = c // 32
+                tot += (Fraction(E2M1_TABLE[qc[i, c]]) * Fraction(2) ** (int(qs[i, b]) - 127)
+                        * Fraction(E2M1_TABLE[kc[j, c]]) * Fraction(2) ** (int(ks[j, b]) - 127))
+            assert S[i, j] == float(tot)
+
+
+def test_fp4_attention_on_grid_values_is_exact_attention():
+    # Q and K already on the MXFP4 grid (each block holds a +-6 * 2^e element), K's mean
+    # exactly 0 (tokens in +- pairs), sm_scale 1: nothing is rounded, so S = Q K^T
+    rng = np.random.default_rng(62)
+    L, H, d = 40, 2, 64
+    grid = np.array(E2M1_TABLE[:8])
+
+    def on_grid(n):
+        v = rng.choice(grid, size=(n, H, d)) * rng.choice([-1.0, 1.0], size=(n, H, d))
+        v[:, :, ::32] = 6.0                                     # the block maximum
+        e = rng.integers(-4, 1, size=(n, H, d // 32))
+        return (v.reshape(n, H, d // 32, 32) * np.exp2(e)[..., None]).reshape(n, H, d)
+    q = on_grid(L)[None].astype(np.float16)
+    half = on_grid(L // 2)
+    k = np.concatenate([half, -half], axis=0)[None].astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    for causal in (False, True):
+        o, qd = O.sage_attn(q, k, v, [L], None, causal, 64, 64, sm_scale=1.0, qk_fp4=True)
+        assert not qd["km"].any()
+        ref = O.exact_attention(q, k, v, [L], None, causal, sm_scale=1.0)
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_fp4_smooth_q_helps_q_with_an_offset():
+    # the page's case for smoothing Q: a 4-bit Q with a per-channel offset keeps
+    # little of the variation; subtracting mean(Q) first restores it
+    rng = np.random.default_rng(63)
+    L, H, d = 256, 2, 64
+    q = (rng.standard_normal((1, L, H, d)) + 4 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    k = (rng.standard_normal((1, L, H, d)) + 2 * rng.standard_normal((1, 1, H, d))).astype(np.float16)
+    v = rng.standard_normal((1, L, H, d)).astype(np.float16)
+    ref = O.exact_attention(q, k, v, [L], None, False)
+    o4, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64, qk_fp4=True)
+    o4s, _ = O.sage_attn(q, k, v, [L], None, False, 64, 64, qk_fp4=True, smooth_q=True)
+    rms = lambda o: float(np.sqrt(np.mean((o - ref) ** 2)))  # noqa: E731
+    assert rms(o4s) < 0.5 * rms(o4)
+    assert cos(o4s, ref) > 0.99 > cos(o4, ref)
