@@ -222,6 +222,18 @@ int sage_debug_qk_i32(const sage_problem* p,
 int sage_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int scale_a, int scale_b, float* d,
                         void* stream);
 
+/* Debug: one issue of the same instruction in its MXFP4 form, the 4-bit Q.K^T
+ * product of the 4-bit variant ([SA2] 技术方案, the INT4 kernel; gfx950's
+ * 4-bit matrix format is OCP MXFP4):
+ *   D[m][n] = C[m][n] + sum_k A[m][k] 2^(scale_a[m][k/32] - 127)
+ *                             * B[k][n] 2^(scale_b[k/32][n] - 127)
+ * A [32][64] and B [64][32] hold one E2M1 code per byte (low nibble);
+ * scale_a [32][2] and scale_b [2][32] are E8M0 codes; C and D fp32 [32][32];
+ * all row-major device arrays (D may not alias the inputs).  One wave;
+ * asynchronous on `stream`. */
+int sage_debug_mxfp4_mfma(const uint8_t* a, const uint8_t* b, const uint8_t* scale_a, const uint8_t* scale_b,
+                          const float* c, float* d, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* sage_last_error(void);
 

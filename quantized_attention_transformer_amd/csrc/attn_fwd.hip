@@ -1061,7 +1061,45 @@ __global__ __launch_bounds__(64) void k_debug_fp8_mfma(const uint8_t* __restrict
   for (int r = 0; r < 16; ++r) Dout[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + m] = acc[r];
 }
 
+// One wave: D = A . B + C with the instruction's MXFP4 form (E2M1 operands,
+// format code 4): lane (m, g) holds A[m][32g .. 32g+31] as 16 bytes, element
+// k in byte k/2 (low nibble first), with its E8M0 scale sa[m][g]; likewise
+// B[32g .. 32g+31][n] with sb[g][n]; each lane's scale applies to its own 32
+// products.  A [32][64] and B [64][32]: one E2M1 code per byte; sa [32][2], sb
+// [2][32] E8M0 codes; C and D fp32 [32][32], all row-major.
+__global__ __launch_bounds__(64) void k_debug_mxfp4_mfma(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                         const uint8_t* __restrict__ SA, const uint8_t* __restrict__ SB,
+                                                         const float* __restrict__ C, float* __restrict__ Dout) {
+  const int lane = threadIdx.x, m = lane & 31, g = lane >> 5;
+  v8i av = {}, bv = {};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t wa = 0, wb = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int k = 32 * g + 8 * j + t;
+      wa |= (uint32_t)(A[m * 64 + k] & 0xF) << (4 * t);
+      wb |= (uint32_t)(B[k * 32 + m] & 0xF) << (4 * t);
+    }
+    av[j] = (int)wa;
+    bv[j] = (int)wb;
+  }
+  const int sa = SA[m * 2 + g], sb = SB[g * 32 + m];
+  v16f acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = C[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + m];
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, sa, 0, sb);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Dout[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + m] = acc[r];
+}
+
 }  // namespace
+
+hipError_t launch_debug_mxfp4_mfma(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                   const float* c, float* d, hipStream_t st) {
+  hipLaunchKernelGGL(k_debug_mxfp4_mfma, dim3(1), dim3(64), 0, st, a, b, sa, sb, c, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
   return p.head_dim == 64 ? launch_d<64>(p, a, causal, fp8, st) : launch_d<128>(p, a, causal, fp8, st);

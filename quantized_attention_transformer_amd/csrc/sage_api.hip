@@ -466,6 +466,14 @@ int sage_debug_qk_i32(const sage_problem* p, const int8_t* q8, sage_strides q8s,
   return SAGE_OK;
 }
 
+int sage_debug_mxfp4_mfma(const uint8_t* a, const uint8_t* b, const uint8_t* scale_a, const uint8_t* scale_b,
+                          const float* c, float* d, void* stream) {
+  if (!a || !b || !scale_a || !scale_b || !c || !d) return fail(SAGE_ERR_INVALID_ARG, "operands must not be NULL");
+  hipError_t e = sage::launch_debug_mxfp4_mfma(a, b, scale_a, scale_b, c, d, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "debug mxfp4 mfma launch");
+  return SAGE_OK;
+}
+
 int sage_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int scale_a, int scale_b, float* d,
                         void* stream) {
   if (!a || !b || !c || !d) return fail(SAGE_ERR_INVALID_ARG, "operands must not be NULL");

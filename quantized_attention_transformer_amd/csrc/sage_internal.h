@@ -90,5 +90,8 @@ hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp
 // One FP8 P.V MFMA on given operands (debug; one wave).
 hipError_t launch_debug_fp8_mfma(const uint8_t* a, const uint8_t* b, const float* c, int sa, int sb, float* d,
                                  hipStream_t st);
+// One MXFP4 MFMA with per-lane E8M0 scales (debug; one wave).
+hipError_t launch_debug_mxfp4_mfma(const uint8_t* a, const uint8_t* b, const uint8_t* sa, const uint8_t* sb,
+                                   const float* c, float* d, hipStream_t st);
 
 }  // namespace sage

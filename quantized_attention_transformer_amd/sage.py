@@ -28,7 +28,8 @@ SAGE_PV_FP8_SMOOTH_V = 2
 EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quantize", "sage_quantize_v_fp8",
             "sage_quantize_v_fp8_smooth_workspace_bytes", "sage_quantize_v_fp8_smooth",
             "sage_quantize_smooth_q_workspace_bytes", "sage_quantize_smooth_q",
-            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma", "sage_last_error")
+            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma",
+            "sage_debug_mxfp4_mfma", "sage_last_error")
 
 
 class Strides(ctypes.Structure):
@@ -69,6 +70,7 @@ def lib():
         L.sage_attn.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp, sz, vp]
         L.sage_debug_qk_i32.argtypes = [P, vp, S, vp, S, vp, vp]
         L.sage_debug_fp8_mfma.argtypes = [vp, vp, vp, i32, i32, vp, vp]
+        L.sage_debug_mxfp4_mfma.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.sage_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
             if name != "sage_last_error":
@@ -296,6 +298,22 @@ def debug_fp8_mfma(a8: torch.Tensor, b8: torch.Tensor, c: torch.Tensor, scale_a:
     d = torch.empty((32, 32), dtype=torch.float32, device=c.device)
     _check("sage_debug_fp8_mfma", lib().sage_debug_fp8_mfma(_ptr(a8), _ptr(b8), _ptr(c), int(scale_a), int(scale_b),
                                                            _ptr(d), _stream()))
+    return d
+
+
+def debug_mxfp4_mfma(a4: torch.Tensor, b4: torch.Tensor, sa: torch.Tensor, sb: torch.Tensor, c: torch.Tensor):
+    """sage_debug_mxfp4_mfma: D = C + sum_k A[m][k] 2^(sa[m][k/32]-127) B[k][n] 2^(sb[k/32][n]-127)
+    on the MXFP4 form of the scaled MFMA.  a4 uint8 [32, 64], b4 uint8 [64, 32] (one E2M1
+    code per byte), sa uint8 [32, 2], sb uint8 [2, 32] (E8M0), c fp32 [32, 32]; returns D."""
+    if a4.shape != (32, 64) or b4.shape != (64, 32) or sa.shape != (32, 2) or sb.shape != (2, 32) \
+            or c.shape != (32, 32):
+        raise ValueError("shapes must be A [32, 64], B [64, 32], sa [32, 2], sb [2, 32], C [32, 32]")
+    if any(t.dtype != torch.uint8 for t in (a4, b4, sa, sb)) or c.dtype != torch.float32:
+        raise ValueError("A, B and the scales are uint8 codes, C is float32")
+    a4, b4, sa, sb, c = (t.contiguous() for t in (a4, b4, sa, sb, c))
+    d = torch.empty((32, 32), dtype=torch.float32, device=c.device)
+    _check("sage_debug_mxfp4_mfma", lib().sage_debug_mxfp4_mfma(_ptr(a4), _ptr(b4), _ptr(sa), _ptr(sb), _ptr(c),
+                                                               _ptr(d), _stream()))
     return d
 
 
