@@ -100,6 +100,8 @@ typedef struct {
   int32_t smooth_q;           /* 1: smooth Q as well (sage_attn and
                                  sage_quantize_smooth_q; blk_k a multiple of 64);
                                  0: not                                           */
+  int32_t qk_fp4;             /* 1: 4-bit Q and K (OCP MXFP4; sage_attn with
+                                 head_dim 128 or 96, sage_quantize_mxfp4); 0: INT8 */
 } sage_problem;
 
 /* Bytes of workspace sage_attn and sage_quantize need for this problem
@@ -140,6 +142,27 @@ int sage_quantize(const sage_problem* p,
  * sage_quantize_smooth_q_workspace_bytes() bytes (column-sum partials of Q
  * and K). */
 int sage_quantize_smooth_q_workspace_bytes(const sage_problem* p, size_t* bytes);
+
+/* 4-bit Q and K ([SA2] 技术方案: the INT4 kernel; gfx950 has no INT4 matrix
+ * instruction, its 4-bit one takes OCP MXFP4):
+ *   K' = fp32(K - k_mean) as in sage_quantize; Q' = fp32(Q * sm_scale), or with
+ *   p->smooth_q Q_s as in sage_quantize_smooth_q (then q_mean and q_delta are
+ *   written as there; otherwise they may be NULL);
+ *   per row and block of 32 channels: e = floor(log2 max|x|) - 2, E8M0 code
+ *   e + 127 (clamped to [0, 254]; 0 for an all-zero block), and E2M1 codes of
+ *   x / 2^e, round to nearest even, saturating at 6, sign bit from x.
+ * q4/k4: the codes two per byte (channel 2c in the low nibble of byte c), rows
+ * of head_dim/2 bytes at the strides q4s/k4s (counted in bytes, multiples of
+ * 16); q_sc/k_sc: one E8M0 byte per block, rows of head_dim/32 bytes at the
+ * strides q_scs/k_scs (bytes).  head_dim 64 or 128.
+ * `workspace` holds sage_quantize_mxfp4_workspace_bytes() bytes. */
+int sage_quantize_mxfp4_workspace_bytes(const sage_problem* p, size_t* bytes);
+int sage_quantize_mxfp4(const sage_problem* p,
+                        const void* Q, sage_strides qs, const void* K, sage_strides ks, float sm_scale,
+                        uint8_t* q4, sage_strides q4s, uint8_t* q_sc, sage_strides q_scs,
+                        uint8_t* k4, sage_strides k4s, uint8_t* k_sc, sage_strides k_scs,
+                        float* k_mean, float* q_mean, float* q_delta,
+                        void* workspace, size_t workspace_bytes, void* stream);
 int sage_quantize_smooth_q(const sage_problem* p,
                            const void* Q, sage_strides qs, const void* K, sage_strides ks, float sm_scale,
                            int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s,
@@ -196,7 +219,10 @@ int sage_attn_quantized(const sage_problem* p,
  * channels 0..95 of O are written.
  * smooth_q = 1: sage_quantize_smooth_q in place of sage_quantize, and the
  * fused kernel adds q_delta to S (a block whose scale is 0 has all codes 0;
- * its S is then the compensation alone). */
+ * its S is then the compensation alone).
+ * qk_fp4 = 1: sage_quantize_mxfp4 in place of sage_quantize and the fused
+ * kernel forms S = Q4 . K4^T on the MXFP4 matrix instruction (the E8M0 scales
+ * applied inside it, fp32 result); blk_q and blk_k are not used. */
 int sage_attn(const sage_problem* p,
               const void* Q, sage_strides qs, const void* K, sage_strides ks,
               const void* V, sage_strides vs, void* out, sage_strides os,

@@ -113,9 +113,10 @@ constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9 (ra
 //                           c ^ 4*((r / 2) % 2) (D = 64)    4 rows x 64 bytes)
 // The E4M3 V is stored transposed ([channel][permuted key], rows of BN+16 bytes).
 // After the key loop the same bytes hold the second half's partial results.
-template <int D, bool FP8>
+template <int D, bool FP8, bool QK4 = false>
 struct Lds {
-  static constexpr int KBYTES = BN * D;
+  static constexpr int KROW = QK4 ? D / 2 : D;  // bytes of a K row (INT8, or MXFP4 codes)
+  static constexpr int KBYTES = BN * KROW;
   static constexpr int VROW = FP8 ? (BN + 16) : 2 * D;
   static constexpr int VBYTES = (FP8 ? D : BN) * VROW;
   static constexpr int VRING = NSK * KBYTES;  // offset of the V ring
@@ -124,12 +125,14 @@ struct Lds {
   static constexpr int MERGE = 4 * MSTRIDE * 64 * 4;
   static constexpr int KSTAB = RING > MERGE ? RING : MERGE;  // per-tile k_scale table (key blocks of 64k keys)
   static constexpr int KSCAP = 4096;                          // its capacity in tiles
-  static constexpr int BYTES = KSTAB + 4 * KSCAP;
+  // (the O staging area after the merge must fit as well: with the 4-bit K tile
+  // and E4M3 V the rings are smaller than it)
+  static constexpr int BYTES0 = KSTAB + 4 * KSCAP;
   // fp16 O rows staged for the stores (after the merge, past the merge area);
   // rows padded by 16 bytes against bank conflicts on the writes
   static constexpr int OROW = 2 * D + 16;
   static constexpr int OSTAGE = MERGE;
-  static_assert(OSTAGE + BM * OROW <= BYTES, "O staging fits the workgroup's LDS");
+  static constexpr int BYTES = BYTES0 > OSTAGE + BM * OROW ? BYTES0 : OSTAGE + BM * OROW;
   // smooth Q: ring of NSD slots of 1 KiB past BYTES, each holding 4 copies of
   // one tile's 64 fp32 compensations
   static constexpr int NSD = 6;
@@ -137,7 +140,7 @@ struct Lds {
   static constexpr int DBYTES = NSD * 1024;
   static constexpr int KCH = KBYTES / 1024;             // 1 KiB DMA blocks per K tile
   static constexpr int VCH = FP8 ? 0 : VBYTES / 1024;   // (fp16 V)
-  __device__ static constexpr int kswz(int r) { return (r / (256 / D)) % (D / 16); }
+  __device__ static constexpr int kswz(int r) { return (r / (256 / KROW)) % (KROW / 16); }
   __device__ static constexpr int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
@@ -177,9 +180,9 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t
 // the swizzle assigns there, at byte offset (row within the tile) *
 // row_stride + 16 * chunk.
 constexpr int NWH = 4;  // waves per half
-template <int D, bool FP8>
+template <int D, bool FP8, bool QK4 = false>
 struct DmaPlan {
-  using S = Lds<D, FP8>;
+  using S = Lds<D, FP8, QK4>;
   static constexpr int KPW = S::KCH / NWH;  // K blocks per wave
   static constexpr int VPW = S::VCH / NWH;  // fp16 V blocks per wave
   static_assert(S::KCH % NWH == 0 && S::VCH % NWH == 0, "tile blocks split over a half");
@@ -191,7 +194,7 @@ struct DmaPlan {
 #pragma unroll
     for (int x = 0; x < KPW; ++x) {
       const int byte = (w + NWH * x) * 1024 + 16 * lane;
-      const int r = byte / D, c = ((byte % D) / 16) ^ S::kswz(r);
+      const int r = byte / S::KROW, c = ((byte % S::KROW) / 16) ^ S::kswz(r);
       koff[x] = (int)(r * kn) + 16 * c;
     }
 #pragma unroll
@@ -306,10 +309,14 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4>
 __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, lds_u8* const lds) {
-  using S = Lds<D, FP8>;
+  using S = Lds<D, FP8, QK4>;
   static_assert(!SQ || KSU, "smooth Q needs key blocks that are multiples of the tile");
+  static_assert(!QK4 || (D == 128 && KSU), "4-bit Q.K^T: head_dim 128, no per-block k-scale table");
+  // 4-bit Q.K^T: the MFMA returns S itself (fp32); INT8: the float 1.5*2^23 + S
+  constexpr float MAG = QK4 ? 0.0f : kMagic;
+  constexpr bool NEGX = SQ || QK4;  // scores may be <= 0: a masked key is -inf
   // Smooth Q: a zero block scale (all codes 0) is replaced.  x' = x + delta /
   // (qs ks) is rounded to fp32, so the unit qs ks must not be coarse next to
   // delta: a zero Q scale becomes 2^-40 (x' then holds delta at fp32 relative
@@ -352,8 +359,23 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int row0 = q0 + (w & 3) * 32;
   const int i = row0 + li;
   v4i qf[D / 32];
-  float qsc = SQ ? kLog2e : 0.0f;  // (rows past the sequence: never stored; smooth Q keeps them finite)
-  if (i < L) {
+  float qsc = (SQ || QK4) ? kLog2e : 0.0f;  // (rows past the sequence: never stored; kept finite)
+  // 4-bit: qf[kk] (kk < D/64) = this lane's 32 E2M1 codes of channels 64kk + 32g .., and
+  // qsb[kk] its block's E8M0 code
+  int qsb[D / 64] = {};
+  if constexpr (QK4) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
+    if (i < L) {
+#pragma unroll
+      for (int kk = 0; kk < D / 64; ++kk)
+        qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
+      const uint32_t wq = *reinterpret_cast<const uint32_t*>(a.qsc4 + seq_head_base(p.cu, a.qss4, s, h) +
+                                                             (int64_t)i * a.qss4.n);
+#pragma unroll
+      for (int kk = 0; kk < D / 64; ++kk) qsb[kk] = (int)((wq >> (8 * (2 * kk + g))) & 0xFFu);
+    }
+  } else if (i < L) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
@@ -362,6 +384,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
   }
+  if constexpr (QK4) qsc = kLog2e;
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
@@ -374,7 +397,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // LDS fragment offsets of this lane: K row li, chunk 2kk+g (swizzled) ...
   uint32_t kofs[D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * D + 16 * ((2 * kk + g) ^ S::kswz(li));
+  for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * S::KROW + 16 * ((2 * kk + g) ^ S::kswz(li));
   const uint32_t vrow8 = li * S::VROW + 32 * g;  // FP8: this lane's V^T row and half
   // ... and the transposed fp16 V reads: rows 4g + tl/4 (+8), chunk 4ct + 2(b&1) + (tl&3)/2
   const int vb = lane >> 4, tl = lane & 15;
@@ -385,9 +408,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     vaddr[ct] = vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
   }
 
-  const bool ks_in_lds = KSU && ntiles <= S::KSCAP;
+  const bool ks_in_lds = KSU && !QK4 && ntiles <= S::KSCAP;
 
-  DmaPlan<D, FP8> dma;
+  DmaPlan<D, FP8, QK4> dma;
   dma.init(w & 3, lane, kn, vn);  // the plan covers a tile with the 4 waves of one half
   V8Stager<D> v8s;
 
@@ -446,9 +469,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     const int j0 = t * BN;
     if constexpr (KSU) {
       // one value per tile, from the LDS table (longer sequences: a scalar
-      // load, counted by lgkmcnt rather than by the tile loads' vmcnt)
-      const float v = qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
-                                       : keff(ksc_c[min(j0, L - 1) / p.blk_k]));
+      // load, counted by lgkmcnt rather than by the tile loads' vmcnt); 4-bit:
+      // the scales are inside S
+      const float v = QK4 ? qsc
+                          : qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
+                                             : keff(ksc_c[min(j0, L - 1) / p.blk_k]));
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -503,7 +528,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // (without smooth Q every real x is > 0, so 0 stands for a masked key)
       auto xv = [&](int jt, int r) {
         const float xx = __int_as_float(sc[jt][r]);
-        if constexpr (MASKED) return valid[jt][r] ? xx : (SQ ? -INFINITY : 0.0f);
+        if constexpr (MASKED) return valid[jt][r] ? xx : (NEGX ? -INFINITY : 0.0f);
         return xx;
       };
       // four independent max3 chains (one wave does all the VALU work of a
@@ -520,7 +545,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       mx = xhalf_max(mx);
       // every real x is >= 1.5*2^23 - 2^21 > 0, so 0 means "all masked": leave m alone
       // (smooth Q: a masked x is -inf, and so is mt)
-      mt = (MASKED && !SQ && mx == 0.0f) ? -INFINITY : (mx - kMagic) * c[0][0];
+      mt = (MASKED && !NEGX && mx == 0.0f) ? -INFINITY : (mx - MAG) * c[0][0];
     } else {
       float mx = -INFINITY;
 #pragma unroll
@@ -559,7 +584,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
     }
     const float mref = FP8 ? m - kLog2_448 : m;  // FP8: P scaled by 448 inside the exponent
-    const float bias = __builtin_fmaf(kMagic, c[0][0], mref);
+    const float bias = __builtin_fmaf(MAG, c[0][0], mref);
     auto prob = [&](int jt, int r) {
       float arg = KSU ? __builtin_fmaf(__int_as_float(sc[jt][r]), c[0][0], -bias) : y[jt][r] - mref;
       if constexpr (MASKED) arg = valid[jt][r] ? arg : -INFINITY;
@@ -619,10 +644,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // 5); ph = b % 5 is advanced at the end of every phase.
   static_assert(NSK == 5 && NSV == 5, "slot arithmetic below");
   int ph = 0;
-  int pd = 0;  // smooth Q: b % 6, the compensation ring (tile t in slot t % 6)
+  int pd = 0;  // smooth Q / 4-bit: b % 6, the rings of per-key data (tile t in slot t % 6)
   auto wrap = [](int x) { return x >= 5 ? x - 5 : x; };
   auto wrap6 = [](int x) { return x >= 6 ? x - 6 : x; };
   auto doffs = [](int slot) { return (uint32_t)(S::DRING + slot * 1024); };
+  // 4-bit: ring of K's per-row E8M0 words (4 copies of a tile's 64 words per slot)
+  auto ksoffs = [](int slot) { return (uint32_t)(S::DRING + (SQ ? S::DBYTES : 0) + slot * 1024); };
   auto koff = [](int slot) { return (uint32_t)(slot * S::KBYTES); };
   auto voff = [](int slot) { return (uint32_t)(S::VRING + slot * S::VBYTES); };
   // Tile loads.  The half that owns tile t (t = hf mod 2) loads K(t) in its
@@ -637,22 +664,27 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int8_t* knext = kseq + (int64_t)hf * BN * kn;
   const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
   // (fp16 V rows hold dv channels: the last row is read up to them only)
-  int krec = (int)((L - 1 - hf * BN) * kn + D), vrec = (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
+  int krec = (int)((L - 1 - hf * BN) * kn + S::KROW), vrec = (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
   // smooth Q: this half's next compensation tile, with K (fp32 per key of this query head)
   const float* dnext = SQ ? a.q_delta + seq_head_base(p.cu, a.qds, s, h) + hf * BN : nullptr;
   int drec = (L - hf * BN) * 4;
   constexpr int dstep = 2 * BN * 4;
+  // 4-bit: this half's next tile of K's E8M0 words (one 32-bit word per key, head kvh)
+  const uint8_t* ksnext = QK4 ? a.ksc4 + seq_head_base(p.cu, a.kss4, s, kvh) + (int64_t)hf * BN * a.kss4.n : nullptr;
+  int ksrec = (L - hf * BN) * 4;
+  const int ksstep = QK4 ? (int)(2 * BN * a.kss4.n) : 0;
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
-  constexpr int KL = DmaPlan<D, FP8>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8>::VPW;
-  constexpr int NOPS = KL + VL + (SQ ? 1 : 0);  // DMA loads per wave per matrix phase
+  constexpr int KL = DmaPlan<D, FP8, QK4>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8, QK4>::VPW;
+  constexpr int NOPS = KL + VL + (SQ ? 1 : 0) + (QK4 ? 1 : 0);  // DMA loads per wave per matrix phase
+  constexpr int QKM = 2 * (QK4 ? D / 64 : D / 32);              // Q.K^T MFMAs per tile
   // Every matrix phase issues NOPS DMA loads per wave (fp16: VL for V, then KL
   // for K, then (smooth Q) one for the compensations; FP8: its V loads to
   // registers come first, then the K and compensation loads).  At the end of a
   // vector phase the loads of the previous matrix phase may stay in flight:
   // s_waitcnt vmcnt(NOPS) (FP8: vmcnt(KL (+1)), its V registers are needed now).
   auto wait_older = [&] {
-    constexpr int n = FP8 ? KL + (SQ ? 1 : 0) : NOPS;
+    constexpr int n = FP8 ? KL + (SQ ? 1 : 0) + (QK4 ? 1 : 0) : NOPS;
     static_assert(n >= 1 && n <= 7, "wait counts below");
     if constexpr (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
@@ -668,6 +700,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // fragments: half h's tiles K(h), K(h+2) and V(h) (empty descriptors past the
   // end) and the per-tile k_scale table.
   for (int x = tid; x < S::RING / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
+  // (and the rings of per-key data: keys past the sequence read what is there, masked)
+  constexpr int NAUX = (SQ ? 1 : 0) + (QK4 ? 1 : 0);
+  for (int x = tid; x < NAUX * S::DBYTES / 16; x += NT) *(LDS v4i*)(lds + S::DRING + 16 * x) = v4i{0, 0, 0, 0};
   __syncthreads();  // the zeroes are in place before any tile lands
   {
     constexpr int KSPT = S::KSCAP / NT;  // k_scale table entries per thread
@@ -693,6 +728,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       dma.issue_d(make_rsrc(dnext + 2 * BN, max(drec - dstep, 0)), lds + doffs(hf + 2));
       dnext += 4 * BN;
       drec -= 2 * dstep;
+    }
+    if constexpr (QK4) {
+      dma.issue_d(make_rsrc(ksnext, max(ksrec, 0)), lds + ksoffs(hf));
+      dma.issue_d(make_rsrc(ksnext + ksstep, max(ksrec - dstep, 0)), lds + ksoffs(hf + 2));
+      ksnext += 2 * ksstep;
+      ksrec -= 2 * dstep;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
@@ -728,31 +769,77 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     ph = wrap(ph + 1);
-    if constexpr (SQ) pd = wrap6(pd + 1);
+    if constexpr (SQ || QK4) pd = wrap6(pd + 1);
   };
   // Matrix phase with every LDS operand read well ahead of its MFMA: all K
   // fragments and the first V group; then the INT8 MFMAs with this phase's
   // tile loads (op(0) .. op(NOPS-1)) issued one per MFMA, in their shadow;
   // then per group of D/32 P.V MFMAs the V reads of the next group.
-  auto qk_pv = [&](uint32_t kso, uint32_t vso, auto&& op) {
+  // 4-bit S^T of one tile (edge phases): K codes from the K slot, K's E8M0 words
+  // from the ring slot kss
+  auto qk4_tile = [&](uint32_t kso, uint32_t kss) {
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const uint32_t wk = *(const LDS uint32_t*)(lds + kss + 4 * (32 * jt + li));
+      v16f acc = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 64; ++kk) {
+        const v4i kv = *(const LDS v4i*)(lds + kso + kofs[kk] + 32 * jt * S::KROW);
+        const v8i ka = __builtin_shufflevector(kv, kv, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v8i qb = __builtin_shufflevector(qf[kk], qf[kk], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, acc, 4, 4, 0,
+                                                              (int)((wk >> (8 * (2 * kk + g))) & 0xFFu), 0, qsb[kk]);
+      }
+      sc[jt] = __builtin_bit_cast(v16i, acc);
+    }
+  };
+  auto qk_pv = [&](uint32_t kso, uint32_t vso, uint32_t kss, auto&& op) {
+    constexpr int KK = QK4 ? D / 64 : D / 32;  // Q.K^T MFMAs per 32-key block
     v4i kf[2][D / 32];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) kf[jt][kk] = *(const LDS v4i*)(lds + kso + kofs[kk] + 32 * jt * D);
+      for (int kk = 0; kk < KK; ++kk) kf[jt][kk] = *(const LDS v4i*)(lds + kso + kofs[kk] + 32 * jt * S::KROW);
+    // 4-bit: the E8M0 code of key 32jt + li, channel block 2kk + g
+    int ksb[2][D / 64] = {};
+    if constexpr (QK4) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const uint32_t wk = *(const LDS uint32_t*)(lds + kss + 4 * (32 * jt + li));
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) ksb[jt][kk] = (int)((wk >> (8 * (2 * kk + g))) & 0xFFu);
+      }
+    }
     // (sched_barrier(0): the instruction order below is the schedule)
     auto qk_mfmas = [&] {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
-        v16i acc = magic;
+        if constexpr (QK4) {
+          v16f acc = {};
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
-          if (jt * (D / 32) + kk < NOPS) op(jt * (D / 32) + kk);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int kk = 0; kk < KK; ++kk) {
+            const v8i ka = __builtin_shufflevector(kf[jt][kk], kf[jt][kk], 0, 1, 2, 3, 4, 5, 6, 7);
+            const v8i qb = __builtin_shufflevector(qf[kk], qf[kk], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, acc, 4, 4, 0, ksb[jt][kk], 0, qsb[kk]);
+            if (jt * KK + kk < NOPS) op(jt * KK + kk);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          sc[jt] = __builtin_bit_cast(v16i, acc);
+        } else {
+          v16i acc = magic;
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
+            if (jt * KK + kk < NOPS) op(jt * KK + kk);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          sc[jt] = acc;
         }
-        sc[jt] = acc;
       }
+    };
+    // tile loads beyond the Q.K^T MFMAs go with the P.V MFMAs
+    auto spill = [&](int x) {
+      if (QKM + x < NOPS) op(QKM + x);
     };
     if constexpr (!FP8) {
       uint32_t va[D / 32];
@@ -775,7 +862,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       for (int u = 0; u < 4; ++u) {
         if (u + 1 < 4) vread(u + 1);
 #pragma unroll
-        for (int ct = 0; ct < D / 32; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u][ct], pf[u], o[ct], 0, 0, 0);
+        for (int ct = 0; ct < D / 32; ++ct) {
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[u][ct], pf[u], o[ct], 0, 0, 0);
+          spill(u * (D / 32) + ct);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -791,9 +881,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       __builtin_amdgcn_sched_barrier(0);
       qk_mfmas();
 #pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct)
+      for (int ct = 0; ct < D / 32; ++ct) {
         o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[ct], pf8, o[ct], 0, 0, 0, 127, 0, pscale);
+        spill(ct);
+      }
     }
+    static_assert(NOPS <= QKM + (FP8 ? D / 32 : D / 8), "every tile load has an MFMA to go with");
   };
   auto mphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
@@ -804,11 +897,16 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     const v4i vr = make_rsrc(vnext, max(vrec, 0)), kr = make_rsrc(knext, max(krec, 0));
     lds_u8* const vsl = lds + voff(wrap(ph + 2));
     lds_u8* const ksl = lds + koff(wrap(ph + 4));
-    v4i dr{};
+    v4i dr{}, ksr{};
     lds_u8* dsl = nullptr;
+    lds_u8* kssl = nullptr;
     if constexpr (SQ) {
       dr = make_rsrc(dnext, max(drec, 0));
       dsl = lds + doffs(wrap6(pd + 4));  // delta(b+4), with K(b+4)
+    }
+    if constexpr (QK4) {
+      ksr = make_rsrc(ksnext, max(ksrec, 0));
+      kssl = lds + ksoffs(wrap6(pd + 4));  // K's E8M0 words of tile b+4, with K(b+4)
     }
     if constexpr (FP8) v8s.load(vseq, vn, (b + 2) * BN, L, tidh);
     auto op = [&](int x) {
@@ -816,16 +914,23 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         dma.issue_v1(vr, vsl, wh, x);
       else if (x < VL + KL)
         dma.issue_k1(kr, ksl, wh, x - VL);
-      else if constexpr (SQ)
+      else if (SQ && x == VL + KL)
         dma.issue_d(dr, dsl);
+      else if constexpr (QK4)
+        dma.issue_d(ksr, kssl);
     };
     if (FULL) {
-      qk_pv(koff(ph), voff(wrap(ph + 3)), op);
+      qk_pv(koff(ph), voff(wrap(ph + 3)), ksoffs(pd), op);
     } else {
 #pragma unroll
       for (int x = 0; x < NOPS; ++x) op(x);
       if (b >= 2 && b - 2 < wtiles) pv(voff(wrap(ph + 3)));
-      if (b < wtiles) qk_tile<D>(lds + koff(ph), kofs, qf, magic, sc);
+      if (b < wtiles) {
+        if constexpr (QK4)
+          qk4_tile(koff(ph), ksoffs(pd));
+        else
+          qk_tile<D>(lds + koff(ph), kofs, qf, magic, sc);
+      }
     }
     knext += kstep;
     krec -= kstep;
@@ -834,6 +939,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     if constexpr (SQ) {
       dnext += 2 * BN;
       drec -= dstep;
+    }
+    if constexpr (QK4) {
+      ksnext += ksstep;
+      ksrec -= dstep;
     }
     end_phase(b, false);
   };
@@ -938,10 +1047,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   }
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4>
 __global__ __launch_bounds__(NT) void k_attn(Problem p, AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[Lds<D, FP8>::BYTES + (SQ ? Lds<D, FP8>::DBYTES : 0)];
-  attn_body<D, FP8, CAUSAL, KSU, SQ>(p, a, (lds_u8*)lds_raw);
+  using S = Lds<D, FP8, QK4>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::BYTES + (SQ ? S::DBYTES : 0) + (QK4 ? S::DBYTES : 0)];
+  attn_body<D, FP8, CAUSAL, KSU, SQ, QK4>(p, a, (lds_u8*)lds_raw);
 }
 
 // Debug: the INT32 scores of the same staging (DmaPlan) and MFMA path
@@ -999,19 +1109,27 @@ __global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
   }
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4 = false>
 hipError_t launch_cfg(const Problem& p, const AttnArgs& a, hipStream_t st) {
   const int nqt = (p.max_seqlen + BM - 1) / BM;
   // slots per XCD: ceil(groups / 8) groups of heads/kv_heads query heads
   const int64_t P8 = ((int64_t)p.nseq * p.kv_heads + 7) / 8 * 8 * (p.heads / p.kv_heads);
   const int64_t G = (int64_t)nqt * P8;
   if (G >= (1ll << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU, SQ>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
+  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU, SQ, QK4>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
   return hipGetLastError();
 }
 
 template <int D, bool FP8, bool CAUSAL>
 hipError_t launch_ks(const Problem& p, const AttnArgs& a, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (a.qsc4) {  // 4-bit Q.K^T (MXFP4), with or without smooth Q
+      return a.q_delta ? launch_cfg<D, FP8, CAUSAL, true, true, true>(p, a, st)
+                       : launch_cfg<D, FP8, CAUSAL, true, false, true>(p, a, st);
+    }
+  } else if (a.qsc4) {
+    return hipErrorInvalidValue;
+  }
   if (a.q_delta) {  // smooth Q (key blocks that are multiples of the tile: checked by the caller)
     if (p.blk_k % BN != 0) return hipErrorInvalidValue;
     return launch_cfg<D, FP8, CAUSAL, true, true>(p, a, st);

@@ -321,8 +321,9 @@ __global__ __launch_bounds__(kQThreads) void k_colsums_qk(const _Float16* __rest
   const int n1 = min(L, n0 + kKSumRows);
   const int cg = threadIdx.x % (D / 8);
   const bool cgv = 8 * cg < dv;
-  colsum_chunk<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, cgv,
-                  qpart + (((int64_t)s * H + h) * nks + ci) * D);
+  if (qpart)
+    colsum_chunk<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, cgv,
+                    qpart + (((int64_t)s * H + h) * nks + ci) * D);
   if (h < kv_heads) {
     __syncthreads();  // (colsum_chunk's LDS is reused)
     colsum_chunk<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, n1, cgv,
@@ -521,6 +522,74 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
   const float scale = quant_block<D>(kb, ks.n, n0, n1, [&](float v, int i) { return v - mean[i]; },
                                      k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n, cgv, pre ? &krows : nullptr);
   if (threadIdx.x == 0) sk[sh * nbk + bi] = scale;
+}
+
+// ---------------------------------------------------------------- MXFP4 Q and K
+// 4-bit Q and K ("4比特量化三倍加速不掉点！清华即插即用的SageAttention迎来升级",
+// 技术方案: the INT4 kernel) in the 4-bit matrix format of gfx950, OCP MXFP4:
+// per row, per block of 32 channels, an E8M0 exponent e = floor(log2 max|x|) - 2
+// (code e + 127, clamped to [0, 254]; 0 for an all-zero block) and E2M1
+// elements RNE(x / 2^e), ties to the even code, saturating at 6, sign bit from
+// x.  x / 2^e is exact (a power-of-two scaling whose result is either normal
+// or far below the smallest E2M1 step).
+
+// E2M1 code of y (|y| compared with the midpoints of 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+// a midpoint goes to the even code).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t mag = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return mag | ((__float_as_uint(y) >> 28) & 0x8u);
+}
+
+// grid (ceil(max_seqlen / RPP), heads, nseq), kQThreads: thread (r, cg) quantises
+// channels 8cg .. 8cg+7 of row x*RPP + r of x' = transform(x) (Q: fp32(Q *
+// sm_scale), minus q_mean when smoothing Q; K: fp32(K - k_mean)); a block of 32
+// channels is 4 neighbouring threads.  Writes the 8 codes as one dword (element
+// c at nibble c) at byte 4cg of the row in x4 (row stride x4s.n bytes) and the
+// block's E8M0 code at byte cg/4 of the row in xsc (row stride xss.n bytes).
+template <int D, bool IS_Q>
+__global__ __launch_bounds__(kQThreads) void k_quant_mxfp4(const _Float16* __restrict__ X, Str xs,
+                                                           const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                           float sm_scale, const float* __restrict__ mean,
+                                                           uint8_t* __restrict__ x4, Str x4s, uint8_t* __restrict__ xsc,
+                                                           Str xss) {
+  constexpr int TPR = D / 8, RPP = kQThreads / TPR;
+  const int h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int L = seq_len(cu, s, max_seqlen);
+  const int tid = threadIdx.x, cg = tid % TPR, n = blockIdx.x * RPP + tid / TPR;
+  if (blockIdx.x * RPP >= L) return;
+  const bool valid = n < L;
+  float mu[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mu[i] = mean ? mean[((int64_t)s * H + h) * D + cg * 8 + i] : 0.0f;
+  float xv[8] = {};
+  float a = 0.0f;
+  if (valid) {
+    const H8 row = load_h8_or_zero(X + seq_head_base(cu, xs, s, h) + (int64_t)n * xs.n + cg * 8, 8 * cg < dv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+      const float v = (float)row.v[i];
+      xv[i] = IS_Q ? (v * sm_scale - mu[i]) : (v - mu[i]);
+      a = fmaxf(a, fabsf(xv[i]));
+    }
+  }
+  a = fmaxf(a, __shfl_xor(a, 1, 64));  // the block's 4 threads
+  a = fmaxf(a, __shfl_xor(a, 2, 64));
+  if (!valid) return;
+  int code = 0;
+  if (a > 0.0f) {
+    int k;
+    (void)frexpf(a, &k);  // a = m 2^k, m in [0.5, 1): floor(log2 a) = k - 1
+    code = min(254, max(0, 127 + (k - 1) - 2));
+  }
+  uint32_t w = 0;
+  if (code > 0 || a > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(xv[i], 127 - code)) << (4 * i);
+  }
+  *reinterpret_cast<uint32_t*>(x4 + seq_head_base(cu, x4s, s, h) + (int64_t)n * x4s.n + 4 * cg) = w;
+  if ((cg & 3) == 0) xsc[seq_head_base(cu, xss, s, h) + (int64_t)n * xss.n + cg / 4] = (uint8_t)code;
 }
 
 // ---------------------------------------------------------------- E4M3 V
@@ -765,6 +834,35 @@ hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const 
       hipLaunchKernelGGL((k_quant_q_smooth<D, false>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
                          p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
     }
+  });
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp4(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                              uint8_t* q4, Str q4s, uint8_t* qsc, Str qss, uint8_t* k4, Str k4s, uint8_t* ksc, Str kss,
+                              float* k_mean, float* q_mean, double* kpart, double* qpart, hipStream_t st) {
+  hipError_t e;
+  SAGE_DISPATCH_D(p.head_dim, {
+    constexpr int RPP = kQThreads / (D / 8);
+    const int nx = (p.max_seqlen + RPP - 1) / RPP;
+    hipLaunchKernelGGL((k_colsums_qk<D>), dim3(p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st, (const _Float16*)Q, qs,
+                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.nks, p.kv_heads, p.dv,
+                       p.smooth_q ? qpart : nullptr, kpart);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st, kpart, p.cu,
+                       p.max_seqlen, p.nks, 1.0, k_mean);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.smooth_q) {
+      hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
+                         p.max_seqlen, p.nks, (double)sm_scale, q_mean);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_quant_mxfp4<D, true>), dim3(nx, p.heads, p.nseq), dim3(kQThreads), 0, st,
+                       (const _Float16*)Q, qs, p.cu, p.max_seqlen, p.dv, sm_scale, p.smooth_q ? q_mean : nullptr, q4,
+                       q4s, qsc, qss);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_quant_mxfp4<D, false>), dim3(nx, p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
+                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.dv, 1.0f, k_mean, k4, k4s, ksc, kss);
   });
   return hipGetLastError();
 }

@@ -58,8 +58,16 @@ int check_problem(const sage_problem* p, bool allow_d96 = false) {
     return fail(SAGE_ERR_INVALID_ARG, "kv_heads (%d) must divide heads (%d) (0: same as heads)", p->kv_heads,
                 p->heads);
   if (p->smooth_q != 0 && p->smooth_q != 1) return fail(SAGE_ERR_INVALID_ARG, "smooth_q must be 0 or 1");
-  if (p->smooth_q && p->blk_k % 64 != 0)
+  if (p->qk_fp4 != 0 && p->qk_fp4 != 1) return fail(SAGE_ERR_INVALID_ARG, "qk_fp4 must be 0 or 1");
+  if (p->smooth_q && !p->qk_fp4 && p->blk_k % 64 != 0)
     return fail(SAGE_ERR_UNSUPPORTED, "smooth_q needs blk_k to be a multiple of 64 (got %d)", p->blk_k);
+  return SAGE_OK;
+}
+
+// Entries that take INT8 Q and K only.
+int no_qk_fp4(const sage_problem* p, const char* name) {
+  if (p->qk_fp4)
+    return fail(SAGE_ERR_UNSUPPORTED, "%s does not take qk_fp4 (use sage_quantize_mxfp4 / sage_attn)", name);
   return SAGE_OK;
 }
 
@@ -88,6 +96,7 @@ sage::Problem to_internal(const sage_problem* p) {
   q.nchunk = (int)cdiv(p->max_seqlen, sage::kColChunk);
   q.nks = (int)cdiv(p->max_seqlen, sage::kKSumRows);
   q.smooth_q = p->smooth_q;
+  q.qk_fp4 = p->qk_fp4;
   return q;
 }
 
@@ -124,6 +133,9 @@ int kv_heads_of(const sage_problem* p) { return p->kv_heads > 0 ? p->kv_heads : 
 struct WsLayout {
   size_t q8, k8, sq, sk, km, colsum, v8, sv, vpsum, vpmax, vpmin, qpart, qm, qdelta, total;
   sage_strides s8q, s8kv, sqd;
+  // 4-bit Q and K: q8/k8 hold the packed codes (rows of d/2 bytes, strides s4q/s4kv in
+  // bytes) and sq/sk the E8M0 codes (rows of d/32 bytes, strides ssq/sskv)
+  sage_strides s4q, s4kv, ssq, sskv;
 };
 
 // Strides of q_delta (one fp32 per (sequence, query head, token)): dense
@@ -166,10 +178,17 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
     off += align_up(bytes);
     return o;
   };
-  w.q8 = take((size_t)(T * H * d));
-  w.k8 = take((size_t)(T * Hk * d));
-  w.sq = take((size_t)p->nseq * H * q.nbq * 4);
-  w.sk = take((size_t)p->nseq * Hk * q.nbk * 4);
+  if (p->qk_fp4) {
+    w.q8 = take((size_t)(T * H * d / 2));
+    w.k8 = take((size_t)(T * Hk * d / 2));
+    w.sq = take((size_t)(T * H * d / 32));
+    w.sk = take((size_t)(T * Hk * d / 32));
+  } else {
+    w.q8 = take((size_t)(T * H * d));
+    w.k8 = take((size_t)(T * Hk * d));
+    w.sq = take((size_t)p->nseq * H * q.nbq * 4);
+    w.sk = take((size_t)p->nseq * Hk * q.nbk * 4);
+  }
   w.km = take((size_t)p->nseq * Hk * d * 4);
   w.colsum = take((size_t)p->nseq * Hk * q.nks * d * 8);
   if (pv_mode == SAGE_PV_FP8 || pv_mode == SAGE_PV_FP8_SMOOTH_V) {
@@ -191,13 +210,17 @@ WsLayout ws_layout(const sage_problem* p, int pv_mode) {
   }
   w.sqd = qdelta_strides(p);
   w.total = off;
-  if (p->cu_seqlens) {
-    w.s8q = sage_strides{0, T * d, d};
-    w.s8kv = w.s8q;
-  } else {
-    w.s8q = sage_strides{H * p->max_seqlen * d, p->max_seqlen * d, d};
-    w.s8kv = sage_strides{Hk * p->max_seqlen * d, p->max_seqlen * d, d};
-  }
+  // head-major rows of `row` bytes: dense [nseq][heads][max_seqlen], packed [heads][T]
+  auto rows = [&](int64_t heads, int64_t row) {
+    return p->cu_seqlens ? sage_strides{0, T * row, row}
+                         : sage_strides{heads * p->max_seqlen * row, p->max_seqlen * row, row};
+  };
+  w.s8q = rows(H, d);
+  w.s8kv = rows(Hk, d);
+  w.s4q = rows(H, d / 2);
+  w.s4kv = rows(Hk, d / 2);
+  w.ssq = rows(H, d / 32);
+  w.sskv = rows(Hk, d / 32);
   return w;
 }
 
@@ -210,6 +233,26 @@ size_t quantize_ws_bytes(const sage_problem* p) {
 size_t quantize_sq_ws_bytes(const sage_problem* p) {
   const sage::Problem q = to_internal(p);
   return quantize_ws_bytes(p) + align_up((size_t)p->nseq * p->heads * q.nks * q.head_dim * 8);
+}
+
+// sage_quantize_mxfp4: K column-sum partials, then (smooth Q) Q's.
+size_t quantize_fp4_ws_bytes(const sage_problem* p) {
+  return p->smooth_q ? quantize_sq_ws_bytes(p) : quantize_ws_bytes(p);
+}
+
+int run_quantize_mxfp4(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                       float sm_scale, uint8_t* q4, sage_strides q4s, uint8_t* qsc, sage_strides qss, uint8_t* k4,
+                       sage_strides k4s, uint8_t* ksc, sage_strides kss, float* k_mean, float* q_mean,
+                       float* q_delta, sage_strides qds, double* kpart, double* qpart, hipStream_t st) {
+  const sage::Problem q = to_internal(p);
+  if (sm_scale <= 0.0f || !std::isfinite(sm_scale)) sm_scale = (float)(1.0 / std::sqrt((double)p->head_dim));
+  hipError_t e;
+  if ((e = sage::launch_quant_mxfp4(q, Q, S(qs), K, S(ks), sm_scale, q4, S(q4s), qsc, S(qss), k4, S(k4s), ksc,
+                                    S(kss), k_mean, q_mean, kpart, qpart, st)) != hipSuccess)
+    return hip_fail(e, "mxfp4 quantisation launch");
+  if (p->smooth_q && (e = sage::launch_q_delta(q, K, S(ks), q_mean, k_mean, q_delta, S(qds), st)) != hipSuccess)
+    return hip_fail(e, "q_delta launch");
+  return SAGE_OK;
 }
 
 int run_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
@@ -274,9 +317,16 @@ extern "C" {
 
 const char* sage_last_error(void) { return g_last_error.c_str(); }
 
+// The fused kernel's 4-bit Q.K^T runs on 128-channel heads (96: padded).
+int fp4_head_dim(const sage_problem* p) {
+  if (p->qk_fp4 && p->head_dim == 64)
+    return fail(SAGE_ERR_UNSUPPORTED, "qk_fp4 attention needs head_dim 128 or 96 (got 64)");
+  return SAGE_OK;
+}
+
 int sage_workspace_bytes(const sage_problem* p, int pv_mode, size_t* bytes) {
   int rc = check_problem(p, true);
-  if (rc) return rc;
+  if (rc || (rc = fp4_head_dim(p))) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = ws_layout(p, pv_mode).total;
@@ -295,7 +345,7 @@ int sage_quantize(const sage_problem* p, const void* Q, sage_strides qs, const v
                   float sm_scale, int8_t* q8, sage_strides q8s, int8_t* k8, sage_strides k8s, float* q_scale,
                   float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
-  if (rc || (rc = no_smooth_q(p, "sage_quantize"))) return rc;
+  if (rc || (rc = no_smooth_q(p, "sage_quantize")) || (rc = no_qk_fp4(p, "sage_quantize"))) return rc;
   if (empty(p)) return SAGE_OK;
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
       (rc = check_tensor("q8", q8, q8s, 16, p)) || (rc = check_tensor("k8", k8, k8s, 16, p)))
@@ -321,7 +371,7 @@ int sage_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs
                            float* k_scale, float* k_mean, float* q_mean, float* q_delta, void* workspace,
                            size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
-  if (rc) return rc;
+  if (rc || (rc = no_qk_fp4(p, "sage_quantize_smooth_q"))) return rc;
   if (!p->smooth_q) return fail(SAGE_ERR_INVALID_ARG, "sage_quantize_smooth_q needs p->smooth_q = 1");
   if (empty(p)) return SAGE_OK;
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
@@ -337,6 +387,38 @@ int sage_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs
   return run_quantize_smooth_q(p, Q, qs, K, ks, sm_scale, q8, q8s, k8, k8s, q_scale, k_scale, k_mean, q_mean, q_delta,
                                qdelta_strides(p), (double*)ws, (double*)(ws + quantize_ws_bytes(p)),
                                (hipStream_t)stream);
+}
+
+int sage_quantize_mxfp4_workspace_bytes(const sage_problem* p, size_t* bytes) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!bytes) return fail(SAGE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = quantize_fp4_ws_bytes(p);
+  return SAGE_OK;
+}
+
+int sage_quantize_mxfp4(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                        float sm_scale, uint8_t* q4, sage_strides q4s, uint8_t* q_sc, sage_strides q_scs, uint8_t* k4,
+                        sage_strides k4s, uint8_t* k_sc, sage_strides k_scs, float* k_mean, float* q_mean,
+                        float* q_delta, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (empty(p)) return SAGE_OK;
+  if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
+      (rc = check_tensor("q4", q4, q4s, 16, p)) || (rc = check_tensor("k4", k4, k4s, 16, p)))
+    return rc;
+  if (!q_sc || !k_sc || q_scs.h < 0 || q_scs.n < 0 || q_scs.s < 0 || k_scs.h < 0 || k_scs.n < 0 || k_scs.s < 0)
+    return fail(SAGE_ERR_INVALID_ARG, "q_sc/k_sc must be non-NULL with non-negative strides");
+  if (!k_mean || (p->smooth_q && (!q_mean || !q_delta)))
+    return fail(SAGE_ERR_INVALID_ARG, "k_mean (and with smooth_q q_mean, q_delta) must not be NULL");
+  const size_t need = quantize_fp4_ws_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char* ws = (char*)workspace;
+  return run_quantize_mxfp4(p, Q, qs, K, ks, sm_scale, q4, q4s, q_sc, q_scs, k4, k4s, k_sc, k_scs, k_mean, q_mean,
+                            q_delta, qdelta_strides(p), (double*)ws,
+                            p->smooth_q ? (double*)(ws + quantize_ws_bytes(p)) : nullptr, (hipStream_t)stream);
 }
 
 int sage_quantize_v_fp8_smooth_workspace_bytes(const sage_problem* p, size_t* bytes) {
@@ -375,7 +457,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
                         sage_strides k8s, const float* q_scale, const float* k_scale, const void* V, sage_strides vs,
                         const float* v_scale, void* out, sage_strides os, int causal, int pv_mode, void* stream) {
   int rc = check_problem(p);
-  if (rc || (rc = no_smooth_q(p, "sage_attn_quantized"))) return rc;
+  if (rc || (rc = no_smooth_q(p, "sage_attn_quantized")) || (rc = no_qk_fp4(p, "sage_attn_quantized"))) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
   const bool fp8 = pv_mode != SAGE_PV_FP16;
@@ -397,7 +479,7 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
               sage_strides vs, void* out, sage_strides os, int causal, float sm_scale, int pv_mode, void* workspace,
               size_t workspace_bytes, void* stream) {
   int rc = check_problem(p, true);
-  if (rc) return rc;
+  if (rc || (rc = fp4_head_dim(p))) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
   if (empty(p)) return SAGE_OK;
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
@@ -414,7 +496,13 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   int8_t* k8 = (int8_t*)(ws + w.k8);
   float* sq = (float*)(ws + w.sq);
   float* sk = (float*)(ws + w.sk);
-  if (p->smooth_q) {
+  if (p->qk_fp4) {
+    if ((rc = run_quantize_mxfp4(p, Q, qs, K, ks, sm_scale, (uint8_t*)q8, w.s4q, (uint8_t*)sq, w.ssq, (uint8_t*)k8,
+                                 w.s4kv, (uint8_t*)sk, w.sskv, (float*)(ws + w.km), (float*)(ws + w.qm),
+                                 (float*)(ws + w.qdelta), w.sqd, (double*)(ws + w.colsum), (double*)(ws + w.qpart),
+                                 st)))
+      return rc;
+  } else if (p->smooth_q) {
     if ((rc = run_quantize_smooth_q(p, Q, qs, K, ks, sm_scale, q8, w.s8q, k8, w.s8kv, sq, sk, (float*)(ws + w.km),
                                     (float*)(ws + w.qm), (float*)(ws + w.qdelta), w.sqd, (double*)(ws + w.colsum),
                                     (double*)(ws + w.qpart), st)))
@@ -441,8 +529,10 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
     vin_s = w.s8kv;
     sv = (const float*)(ws + w.sv);
   }
-  sage::AttnArgs a{q8, S(w.s8q), k8, S(w.s8kv), sq, sk, vin, S(vin_s), sv, out, S(os), nullptr, vmean,
-                   p->smooth_q ? (const float*)(ws + w.qdelta) : nullptr, S(w.sqd)};
+  sage::AttnArgs a{q8, S(p->qk_fp4 ? w.s4q : w.s8q), k8, S(p->qk_fp4 ? w.s4kv : w.s8kv), sq, sk, vin, S(vin_s), sv,
+                   out, S(os), nullptr, vmean, p->smooth_q ? (const float*)(ws + w.qdelta) : nullptr, S(w.sqd),
+                   p->qk_fp4 ? (const uint8_t*)sq : nullptr, S(w.ssq), p->qk_fp4 ? (const uint8_t*)sk : nullptr,
+                   S(w.sskv)};
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode != SAGE_PV_FP16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;

@@ -36,6 +36,7 @@ struct Problem {
   int nbq, nbk, nchunk;  // ceil(max_seqlen/blk_q), ceil(max_seqlen/blk_k), ceil(max_seqlen/kColChunk)
   int nks;               // ceil(max_seqlen/kKSumRows): K column-sum partials per (sequence, head)
   int smooth_q;          // Q smoothed by its mean; S compensated by q_delta (key blocks: multiples of 64)
+  int qk_fp4;            // 4-bit (MXFP4) Q and K
 };
 
 // ---- pre-pass (prepass.hip) ----
@@ -52,6 +53,13 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
 hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, float* q_mean, double* qpart, double* kpart,
                                  hipStream_t st);
+// 4-bit Q and K (MXFP4): column sums of K (and, smooth_q, of Q; partials as above), k_mean
+// (q_mean) finalised, then per row and block of 32 channels an E8M0 code (byte cg/4 of the row
+// in qsc/ksc, row stride .n bytes) and the E2M1 codes packed two per byte, low nibble first
+// (q4/k4, row stride .n bytes), of Q' = fp32(Q * sm_scale) (- q_mean) and K' = fp32(K - k_mean).
+hipError_t launch_quant_mxfp4(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
+                              uint8_t* q4, Str q4s, uint8_t* qsc, Str qss, uint8_t* k4, Str k4s, uint8_t* ksc, Str kss,
+                              float* k_mean, float* q_mean, double* kpart, double* qpart, hipStream_t st);
 // q_delta[s, h, n] = q_mean[s, h] . fp32(K[s, kvh(h), n] - k_mean[s, kvh(h)]) (fp64 sum, fp32 result);
 // element (s, h, n) at seq_head_base(cu, qds, s, h) + n.
 hipError_t launch_q_delta(const Problem& p, const void* K, Str ks, const float* q_mean, const float* k_mean,
@@ -85,6 +93,12 @@ struct AttnArgs {
   const float* v_mean;  // FP8 with smoothed V: per-channel mean added to O, else nullptr
   const float* q_delta;  // smooth Q: per (sequence, query head, key) compensation added to S, else nullptr
   Str qds;               // its strides (n = 1)
+  // 4-bit Q.K^T (MXFP4; head_dim 128): q8/k8 then hold E2M1 codes, two per byte (rows of
+  // head_dim/2 bytes), and these the E8M0 codes, 4 bytes per row (strides in bytes); else nullptr
+  const uint8_t* qsc4;
+  Str qss4;
+  const uint8_t* ksc4;
+  Str kss4;
 };
 hipError_t launch_attn(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
 // One FP8 P.V MFMA on given operands (debug; one wave).

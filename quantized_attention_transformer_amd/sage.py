@@ -28,6 +28,7 @@ SAGE_PV_FP8_SMOOTH_V = 2
 EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quantize", "sage_quantize_v_fp8",
             "sage_quantize_v_fp8_smooth_workspace_bytes", "sage_quantize_v_fp8_smooth",
             "sage_quantize_smooth_q_workspace_bytes", "sage_quantize_smooth_q",
+            "sage_quantize_mxfp4_workspace_bytes", "sage_quantize_mxfp4",
             "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma",
             "sage_debug_mxfp4_mfma", "sage_last_error")
 
@@ -40,7 +41,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("nseq", ctypes.c_int32), ("heads", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("total_tokens", ctypes.c_int64), ("cu_seqlens", ctypes.c_void_p),
                 ("blk_q", ctypes.c_int32), ("blk_k", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
-                ("smooth_q", ctypes.c_int32)]
+                ("smooth_q", ctypes.c_int32), ("qk_fp4", ctypes.c_int32)]
 
 
 class SageError(RuntimeError):
@@ -63,6 +64,8 @@ def lib():
         L.sage_quantize.argtypes = [P, vp, S, vp, S, f32, vp, S, vp, S, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_smooth_q_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
         L.sage_quantize_smooth_q.argtypes = [P, vp, S, vp, S, f32, vp, S, vp, S, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sage_quantize_mxfp4_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+        L.sage_quantize_mxfp4.argtypes = [P, vp, S, vp, S, f32, vp, S, vp, S, vp, S, vp, S, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_v_fp8.argtypes = [P, vp, S, vp, S, vp, vp]
         L.sage_quantize_v_fp8_smooth_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
         L.sage_quantize_v_fp8_smooth.argtypes = [P, vp, S, vp, S, vp, vp, sz, vp]
@@ -207,6 +210,40 @@ def quantize_smooth_q(q, k, *, sm_scale: Optional[float] = None, layout="bnhd", 
     return dict(q8=q8, k8=k8, q_scale=sq, k_scale=sk, k_mean=km, q_mean=qm, q_delta=qdel)
 
 
+def quantize_mxfp4(q, k, *, sm_scale: Optional[float] = None, layout="bnhd", cu_seqlens=None, max_seqlen=None,
+                   smooth_q=False):
+    """sage_quantize_mxfp4: 4-bit (MXFP4) Q and K.  Returns dict(q4, k4 (uint8, two E2M1
+    codes per byte, the shapes of q and k with d/2 channels), q_scale, k_scale (uint8 E8M0
+    codes, d/32 per row), k_mean, and with smooth_q q_mean and q_delta)."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, k=k)
+    prob.smooth_q = int(bool(smooth_q))
+    d = prob.head_dim
+    q4 = torch.empty(q.shape[:-1] + (d // 2,), dtype=torch.uint8, device=q.device)
+    k4 = torch.empty(k.shape[:-1] + (d // 2,), dtype=torch.uint8, device=q.device)
+    qsc = torch.zeros(q.shape[:-1] + (d // 32,), dtype=torch.uint8, device=q.device)
+    ksc = torch.zeros(k.shape[:-1] + (d // 32,), dtype=torch.uint8, device=q.device)
+    nseq, H, N = prob.nseq, prob.heads, prob.max_seqlen
+    Hk = prob.kv_heads or H
+    km = torch.zeros((nseq, Hk, d), dtype=torch.float32, device=q.device)
+    qm = torch.zeros((nseq, H, d), dtype=torch.float32, device=q.device)
+    qdel = torch.zeros((H, prob.total_tokens) if cu_seqlens is not None else (nseq, H, N), dtype=torch.float32,
+                       device=q.device)
+    n = ctypes.c_size_t(0)
+    _check("sage_quantize_mxfp4_workspace_bytes",
+           lib().sage_quantize_mxfp4_workspace_bytes(ctypes.byref(prob), ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    rc = lib().sage_quantize_mxfp4(ctypes.byref(prob), _ptr(q), strides_of(q, layout), _ptr(k), strides_of(k, layout),
+                                   0.0 if sm_scale is None else float(sm_scale), _ptr(q4), strides_of(q4, layout),
+                                   _ptr(qsc), strides_of(qsc, layout), _ptr(k4), strides_of(k4, layout), _ptr(ksc),
+                                   strides_of(ksc, layout), _ptr(km), _ptr(qm), _ptr(qdel), _ptr(ws), ws.numel(),
+                                   _stream())
+    _check("sage_quantize_mxfp4", rc)
+    out = dict(q4=q4, k4=k4, q_scale=qsc, k_scale=ksc, k_mean=km)
+    if smooth_q:
+        out.update(q_mean=qm, q_delta=qdel)
+    return out
+
+
 def quantize_v_fp8(v, *, layout="bnhd", cu_seqlens=None, max_seqlen=None, smooth=False):
     """sage_quantize_v_fp8: returns (v8 uint8 E4M3 codes in v's shape, v_scale [nseq, H, d]).
     smooth=True: sage_quantize_v_fp8_smooth, returns (v8 of the smoothed V, v_scale_mean
@@ -246,12 +283,14 @@ def attn_quantized(q8, k8, q_scale, k_scale, v, *, v_scale=None, causal=False, p
 
 
 def attn(q, k, v, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAGE_PV_FP16, layout="bnhd",
-         cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None, workspace=None, smooth_q=False):
+         cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, out=None, workspace=None, smooth_q=False,
+         qk_fp4=False):
     """sage_attn: the whole forward pass; returns O (fp16, q's shape).  k and v may have
     fewer heads than q (grouped-query attention).  smooth_q: smooth Q as well (blk_k a
-    multiple of 64)."""
+    multiple of 64).  qk_fp4: 4-bit (MXFP4) Q and K (head_dim 128 or 96)."""
     prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k, k=k)
     prob.smooth_q = int(bool(smooth_q))
+    prob.qk_fp4 = int(bool(qk_fp4))
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
     nws = workspace_bytes(prob, pv_mode)
@@ -318,7 +357,8 @@ def debug_mxfp4_mfma(a4: torch.Tensor, b4: torch.Tensor, sa: torch.Tensor, sb: t
 
 
 def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
-                                 enable_gqa=False, *, pv_mode=SAGE_PV_FP16, blk_q=128, blk_k=64, smooth_q=False):
+                                 enable_gqa=False, *, pv_mode=SAGE_PV_FP16, blk_q=128, blk_k=64, smooth_q=False,
+                                 qk_fp4=False):
     """Drop-in for torch.nn.functional.scaled_dot_product_attention on [B, H, N, d]
     fp16 tensors (the interface the SageAttention pages replace in one line):
     softmax(Q K^T * scale) V through sage_attn, with scale = 1/sqrt(d) when None
@@ -344,4 +384,4 @@ def scaled_dot_product_attention(query, key, value, attn_mask=None, dropout_p=0.
     to16 = lambda t: t if (t.dtype == torch.float16 and t.stride(-1) == 1) else t.to(torch.float16).contiguous()  # noqa: E731
     q, k, v = to16(query), to16(key), to16(value)
     return attn(q, k, v, causal=bool(is_causal), sm_scale=None if scale is None else float(scale), pv_mode=pv_mode,
-                layout="bhnd", blk_q=blk_q, blk_k=blk_k, smooth_q=smooth_q)
+                layout="bhnd", blk_q=blk_q, blk_k=blk_k, smooth_q=smooth_q, qk_fp4=qk_fp4)

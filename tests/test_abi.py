@@ -78,6 +78,8 @@ def test_workspace_bytes_layout():
     (dict(kv_heads=3), -1),
     (dict(kv_heads=-1), -1),
     (dict(smooth_q=2), -1),
+    (dict(qk_fp4=2), -1),
+    (dict(qk_fp4=1, head_dim=64), -2),
     (dict(smooth_q=1, blk_k=16), -2),
     (dict(blk_k=512), -1),
     (dict(blk_k=0), -1),
@@ -247,3 +249,32 @@ def test_smooth_q_workspace_and_entry_rules():
     r = sage.lib().sage_quantize_smooth_q(ctypes.byref(p), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE,
                                           FAKE, FAKE, FAKE, FAKE, m.value - 1, None)
     assert r == -3
+
+
+def test_qk_fp4_workspace_and_entry_rules():
+    # 4-bit Q and K (head_dim 128): packed codes (d/2 bytes per row) and one E8M0 byte per
+    # 32 channels in place of the INT8 rows and block scales
+    p = _prob(head_dim=128, qk_fp4=1)
+    rc, n = _ws(p)
+    assert rc == 0
+    # q4 2x256x64, k4 2x256x64, scales 2x256x4 each, k_mean 2x128 floats, K column-sum
+    # partials 2 heads x 2 chunks x 128 channels x 8 bytes
+    assert n == 32768 + 32768 + 2048 + 2048 + 1024 + 4096
+    m = ctypes.c_size_t(0)
+    assert sage.lib().sage_quantize_mxfp4_workspace_bytes(ctypes.byref(p), ctypes.byref(m)) == 0
+    assert m.value == 4096
+    assert sage.lib().sage_quantize_mxfp4_workspace_bytes(ctypes.byref(_prob(head_dim=128, qk_fp4=1, smooth_q=1)),
+                                                        ctypes.byref(m)) == 0
+    assert m.value == 8192
+    st = _strides()
+    r = sage.lib().sage_quantize(ctypes.byref(p), FAKE, st, FAKE, st, 0.0, FAKE, st, FAKE, st, FAKE, FAKE, FAKE,
+                                 FAKE, 1 << 20, None)
+    assert r == -2 and "qk_fp4" in sage.lib().sage_last_error().decode()
+    r = sage.lib().sage_attn_quantized(ctypes.byref(p), FAKE, st, FAKE, st, FAKE, FAKE, FAKE, st, FAKE, FAKE, st,
+                                       0, 0, None)
+    assert r == -2
+    # the quantiser itself takes head_dim 64 too; missing scale outputs are refused
+    p64 = _prob(qk_fp4=1)
+    r = sage.lib().sage_quantize_mxfp4(ctypes.byref(p64), FAKE, st, FAKE, st, 0.0, FAKE, st, None, st, FAKE, st,
+                                       FAKE, st, FAKE, None, None, FAKE, 1 << 20, None)
+    assert r == -1 and "q_sc" in sage.lib().sage_last_error().decode()
