@@ -16,7 +16,8 @@ non-causal and causal), the sage_quantize pre-pass against the HBM peak
 sage_attn end to end (its own workspace).  inputs_sha256 = provenance of
 the synthetic fp16 Q, K, V.
 extra = kernel-only TOPS of the fused kernel on the larger workloads, and
-sage_attn end to end (pre-pass included) plain and with Q smoothed on one.
+sage_attn end to end (pre-pass included) plain, with Q smoothed, and with 4-bit
+(MXFP4) Q and K on one.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -259,7 +260,9 @@ def extra_workloads(sage, torch, dev):
              ("gqa causal B1 H32 kv8 N8192 d128", synth.LONG, True, 0, "gqa"),
              # whole forward pass (sage_attn: pre-pass + fused kernel), plain and with Q smoothed
              ("sage_attn fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "e2e"),
-             ("sage_attn smooth-Q fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "sq")]
+             ("sage_attn smooth-Q fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "sq"),
+             ("sage_attn 4-bit QK (MXFP4) fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "fp4"),
+             ("sage_attn 4-bit QK (MXFP4) FP8-PV B4 H16 N8192 d128", synth.FP8, False, 1, "fp4")]
     for name, wl, causal, mode, kind in cases:
         g.manual_seed(wl.seed)
         if kind == "varlen":
@@ -289,15 +292,16 @@ def extra_workloads(sage, torch, dev):
         vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
         out = torch.empty_like(q)
         ws = None
-        if kind in ("e2e", "sq"):
+        if kind in ("e2e", "sq", "fp4"):
             prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k)
             prob.smooth_q = int(kind == "sq")
+            prob.qk_fp4 = int(kind == "fp4")
             ws = torch.empty(sage.workspace_bytes(prob, mode), dtype=torch.uint8, device=dev)
 
         def run():
             if ws is not None:
                 sage.attn(q, k, v, causal=causal, pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out,
-                          workspace=ws, smooth_q=(kind == "sq"))
+                          workspace=ws, smooth_q=(kind == "sq"), qk_fp4=(kind == "fp4"))
                 return
             sage.attn_quantized(qd["q8"], qd["k8"], qd["q_scale"], qd["k_scale"], vv, v_scale=sv, causal=causal,
                                 pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out, **kw)
