@@ -201,7 +201,8 @@ int sage_quantize_v_fp8_smooth(const sage_problem* p, const void* V, sage_stride
  *   (as written by sage_quantize_v_fp8_smooth); the epilogue adds the mean,
  *   exact since every row of softmax(S) sums to 1.  O is written as fp16 with
  *   strides os; rows of a sequence of length 0 are not written.  Problems
- *   with smooth_q set go through sage_attn (SAGE_ERR_UNSUPPORTED here). */
+ *   with smooth_q set go through sage_attn (SAGE_ERR_UNSUPPORTED here).
+ *   In the FP8 modes v_scale must be 16-byte aligned. */
 int sage_attn_quantized(const sage_problem* p,
                         const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
                         const float* q_scale, const float* k_scale,

@@ -990,9 +990,25 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 
   // ---- merge the halves: half 1 leaves (O^T, m_ref, l) in LDS, half 0 combines.
   // m_ref is the exponent O and l are relative to (fp16: m; FP8: m0), -inf
-  // if this half saw no key of the row.
-  float* const mg = (float*)lds + (w & 3) * S::MSTRIDE * 64 + lane;
+  // if this half saw no key of the row.  O^T goes as 16-byte pieces: piece j
+  // (accumulators 4j .. 4j+3) of lane l at float (4j * 64 + 4l) of the wave's
+  // area (a wave's 64 lanes cover 1 KiB per piece: conflict-free).
+  float* const mgw = (float*)lds + (w & 3) * S::MSTRIDE * 64;
+  float* const mg = mgw + lane;
   const float mref_own = m == -INFINITY ? -INFINITY : (FP8 ? m0 : m);
+  // FP8: the channel scales (and means) of this lane's pieces, loaded now so
+  // that their latency overlaps the merge
+  v4f vsc[FP8 ? D / 8 : 1], vmu[FP8 ? D / 8 : 1];
+  if constexpr (FP8) {
+    if (hf == 0) {
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) {
+        const int cc = 32 * (j / 4) + 8 * (j % 4) + 4 * g;
+        vsc[j] = *reinterpret_cast<const v4f*>(a.v_scale + skv * D + cc);
+        vmu[j] = a.v_mean ? *reinterpret_cast<const v4f*>(a.v_mean + skv * D + cc) : v4f{0, 0, 0, 0};
+      }
+    }
+  }
   // the last matrix phases' loads (past the last tile) are still in flight and
   // write into the ring, which the partial results reuse
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1001,7 +1017,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mg[(16 * ct + r) * 64] = o[ct][r];
+      for (int q = 0; q < 4; ++q)
+        *(LDS v4f*)(mgw + (4 * ct + q) * 256 + 4 * lane) =
+            v4f{o[ct][4 * q], o[ct][4 * q + 1], o[ct][4 * q + 2], o[ct][4 * q + 3]};
     mg[(D / 2) * 64] = mref_own;
     mg[(D / 2 + 1) * 64] = lsum;
   }
@@ -1022,15 +1040,13 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int cc = 32 * ct + 8 * q + 4 * g;
+      const v4f ob = *(const LDS v4f*)(mgw + (4 * ct + q) * 256 + 4 * lane);
       float f[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        f[e] = (o[ct][r] * wa + mg[(16 * ct + r) * 64] * wb) * inv;
-        if constexpr (FP8) {
-          f[e] *= a.v_scale[skv * D + cc + e];
-          if (a.v_mean) f[e] += a.v_mean[skv * D + cc + e];  // smoothed V: P (V - mean) + mean
-        }
+        f[e] = (o[ct][r] * wa + ob[e] * wb) * inv;
+        if constexpr (FP8) f[e] = f[e] * vsc[4 * ct + q][e] + vmu[4 * ct + q][e];  // smoothed V: P (V - mean) + mean
       }
       const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
       *(LDS v4h*)(ostage + (i - q0) * S::OROW + 2 * cc) = hv;

@@ -465,6 +465,7 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
       (rc = check_tensor("V", V, vs, fp8 ? 16 : 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
     return rc;
   if (!q_scale || !k_scale || (fp8 && !v_scale)) return fail(SAGE_ERR_INVALID_ARG, "scales must not be NULL");
+  if (fp8 && !aligned16(v_scale)) return fail(SAGE_ERR_INVALID_ARG, "v_scale must be 16-byte aligned");
   if ((rc = check_row_span("k8", k8s, 1, p)) || (rc = check_row_span("V", vs, fp8 ? 1 : 2, p))) return rc;
   const float* v_mean =
       pv_mode == SAGE_PV_FP8_SMOOTH_V ? v_scale + (size_t)p->nseq * kv_heads_of(p) * p->head_dim : nullptr;
