@@ -363,6 +363,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // 4-bit: qf[kk] (kk < D/64) = this lane's 32 E2M1 codes of channels 64kk + 32g .., and
   // qsb[kk] its block's E8M0 code
   int qsb[D / 64] = {};
+  // The Q scale (word) is loaded here and only used after the prologue's wait,
+  // so that its latency and the fragments' overlap the first tile loads.
+  float qraw = 0.0f;
+  uint32_t wq = 0;
   if constexpr (QK4) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
@@ -370,21 +374,17 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk)
         qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
-      const uint32_t wq = *reinterpret_cast<const uint32_t*>(a.qsc4 + seq_head_base(p.cu, a.qss4, s, h) +
-                                                             (int64_t)i * a.qss4.n);
-#pragma unroll
-      for (int kk = 0; kk < D / 64; ++kk) qsb[kk] = (int)((wq >> (8 * (2 * kk + g))) & 0xFFu);
+      wq = *reinterpret_cast<const uint32_t*>(a.qsc4 + seq_head_base(p.cu, a.qss4, s, h) + (int64_t)i * a.qss4.n);
     }
   } else if (i < L) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
-    qsc = qeff(a.q_scale[sh * p.nbq + i / p.blk_q]) * kLog2e;
+    qraw = a.q_scale[sh * p.nbq + i / p.blk_q];
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
   }
-  if constexpr (QK4) qsc = kLog2e;
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
@@ -703,7 +703,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // (and the rings of per-key data: keys past the sequence read what is there, masked)
   constexpr int NAUX = (SQ ? 1 : 0) + (QK4 ? 1 : 0);
   for (int x = tid; x < NAUX * S::DBYTES / 16; x += NT) *(LDS v4i*)(lds + S::DRING + 16 * x) = v4i{0, 0, 0, 0};
-  __syncthreads();  // the zeroes are in place before any tile lands
+  // The zeroes are in place before any tile lands: this wave's LDS stores are
+  // complete, then the barrier.  (Not __syncthreads: its fence would also wait
+  // for the Q fragments and Q scale loaded above, whose latency should overlap
+  // the tile loads below; the wait at the end of the prologue drains them.)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   {
     constexpr int KSPT = S::KSCAP / NT;  // k_scale table entries per thread
     float ksv[KSPT];
@@ -749,6 +753,14 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // they would also wait for the tile loads it does not see.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
+  asm volatile("" : "+v"(qraw), "+v"(wq));
+  if constexpr (QK4) {
+    qsc = kLog2e;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) qsb[kk] = (int)((wq >> (8 * (2 * kk + g))) & 0xFFu);
+  } else if (i < L) {
+    qsc = qeff(qraw) * kLog2e;
+  }
 
   // ---- phases b = 0 .. ntiles+1, in pairs.  Matrix phase b: S of tile b and
   // P.V of tile b-2, and the loads V(b+2), K(b+4); vector phase b: softmax of
