@@ -1046,20 +1046,25 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // v_scale).  A lane holds 4-channel pieces of its row; the fp16 rows go
   // through LDS so that the stores write whole rows (16 lanes per row).
   const float inv = 1.0f / xhalf_sum(lsum * wa + lsum_b * wb);
+  const float ca = wa * inv, cb = wb * inv;
   lds_u8* const ostage = lds + S::OSTAGE;
+  // all of half 1's pieces first (the O staging writes below could alias them
+  // as far as the compiler knows, which would serialise read, wait and write)
+  v4f ob[D / 8];
+#pragma unroll
+  for (int j = 0; j < D / 8; ++j) ob[j] = *(const LDS v4f*)(mgw + j * 256 + 4 * lane);
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int cc = 32 * ct + 8 * q + 4 * g;
-      const v4f ob = *(const LDS v4f*)(mgw + (4 * ct + q) * 256 + 4 * lane);
       float f[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * q + e;
-        f[e] = (o[ct][r] * wa + ob[e] * wb) * inv;
+        f[e] = o[ct][r] * ca + ob[4 * ct + q][e] * cb;
         if constexpr (FP8) f[e] = f[e] * vsc[4 * ct + q][e] + vmu[4 * ct + q][e];  // smoothed V: P (V - mean) + mean
       }
+      const int cc = 32 * ct + 8 * q + 4 * g;
       const v4h hv = {(_Float16)f[0], (_Float16)f[1], (_Float16)f[2], (_Float16)f[3]};
       *(LDS v4h*)(ostage + (i - q0) * S::OROW + 2 * cc) = hv;
     }
