@@ -695,19 +695,23 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   };
 
-  // ---- prologue.  LDS starts zeroed, so bytes the tail tiles leave untouched
-  // are finite; then, in one batch of loads in flight together with the Q
-  // fragments: half h's tiles K(h), K(h+2) and V(h) (empty descriptors past the
-  // end) and the per-tile k_scale table.
-  for (int x = tid; x < S::RING / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
-  // (and the rings of per-key data: keys past the sequence read what is there, masked)
-  constexpr int NAUX = (SQ ? 1 : 0) + (QK4 ? 1 : 0);
-  for (int x = tid; x < NAUX * S::DBYTES / 16; x += NT) *(LDS v4i*)(lds + S::DRING + 16 * x) = v4i{0, 0, 0, 0};
-  // The zeroes are in place before any tile lands: this wave's LDS stores are
-  // complete, then the barrier.  (Not __syncthreads: its fence would also wait
-  // for the Q fragments and Q scale loaded above, whose latency should overlap
-  // the tile loads below; the wait at the end of the prologue drains them.)
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // ---- prologue.  With a partial last tile the fp16 V ring starts zeroed:
+  // the rows of that tile past the sequence are never loaded, and their
+  // (masked, P = 0) keys must still meet finite V.  Everything else a masked
+  // key reads may be anything: K codes are finite by construction, the E4M3 V
+  // goes through registers with its rows clamped to the sequence, and scores
+  // of masked keys are replaced, not scaled.  Then, in one batch of loads in
+  // flight together with the Q fragments: half h's tiles K(h), K(h+2) and V(h)
+  // (empty descriptors past the end) and the per-tile k_scale table.
+  if (!FP8 && (L % BN) != 0) {
+    for (int x = tid; x < NSV * S::VBYTES / 16; x += NT) *(LDS v4i*)(lds + S::VRING + 16 * x) = v4i{0, 0, 0, 0};
+    // The zeroes are in place before any tile lands: this wave's LDS stores
+    // are complete, then the barrier (the branch is the same for the whole
+    // workgroup).  Not __syncthreads: its fence would also wait for the Q
+    // fragments and Q scale loaded above, whose latency should overlap the
+    // tile loads below; the wait at the end of the prologue drains them.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
   {
     constexpr int KSPT = S::KSCAP / NT;  // k_scale table entries per thread
     float ksv[KSPT];
@@ -1071,12 +1075,17 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   __syncthreads();  // (half 1 has ended: the barrier waits for half 0's waves)
   _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h);
   constexpr int CPR = D / 8;  // 16-byte pieces per row
+  constexpr int NPC = BM * CPR / (NT / 2);
+  v4i opc[NPC];  // (all LDS reads first, then the stores)
 #pragma unroll
-  for (int x = 0; x < BM * CPR / (NT / 2); ++x) {
+  for (int x = 0; x < NPC; ++x) {
     const int c = tid + x * (NT / 2), rr = c / CPR, cp = c % CPR;
-    if (q0 + rr < L && 8 * cp < p.dv)
-      *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) =
-          *(const LDS v4i*)(ostage + rr * S::OROW + 16 * cp);
+    opc[x] = *(const LDS v4i*)(ostage + rr * S::OROW + 16 * cp);
+  }
+#pragma unroll
+  for (int x = 0; x < NPC; ++x) {
+    const int c = tid + x * (NT / 2), rr = c / CPR, cp = c % CPR;
+    if (q0 + rr < L && 8 * cp < p.dv) *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) = opc[x];
   }
 }
 
