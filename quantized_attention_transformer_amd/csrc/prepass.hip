@@ -80,18 +80,24 @@ constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: M + r for an integer |r| <
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 // Rows of a block of up to 128 rows held in registers: thread (r, cg) holds
-// rows n0 + r + RPP*j, j < R, channels 8cg .. 8cg+7.  All loads are issued
-// before any is used, so the block costs one memory round trip.
+// rows n0 + r + RPP*j, j < R, channels 8cg .. 8cg+7 (n0 < n1).  All loads are
+// issued before any is used, so the block costs one memory round trip: a
+// slot past the block's end re-reads row n1 - 1 (callers skip those slots).
+// Branching around such loads instead puts a wait for each load at the end
+// of its branch (the compiler settles pending loads where paths join), which
+// turns the R loads into R round trips.
 template <int D>
 struct BlockRows {
   static constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
   H8 x[R];
   __device__ __forceinline__ void load(const _Float16* __restrict__ src, int64_t sn, int n0, int n1, bool cgv) {
     const int r = threadIdx.x / TPR;
+    if (cgv) {
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const int n = n0 + r + RPP * j;
-      if (n < n1) x[j] = load_h8_or_zero(src + (int64_t)n * sn, cgv);
+      for (int j = 0; j < R; ++j) x[j] = load_h8(src + (int64_t)min(n0 + r + RPP * j, n1 - 1) * sn);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j) *reinterpret_cast<uint4*>(&x[j]) = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 };
@@ -616,11 +622,14 @@ __global__ __launch_bounds__(kThreads) void k_v_colmax(const _Float16* __restric
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
   float m[8] = {};
+  if (8 * cg < dv) {  // padding channels (head_dim 96) keep 0; the test stays outside the loop so that
+                      // the unrolled loads issue together
 #pragma unroll 4
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8_or_zero(base + (int64_t)n * vs.n, 8 * cg < dv);
+    for (int n = n0 + r; n < n1; n += RPP) {
+      const H8 x = load_h8(base + (int64_t)n * vs.n);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf((float)x.v[i]));
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf((float)x.v[i]));
+    }
   }
   __shared__ float red[RPP][D];
 #pragma unroll
@@ -661,9 +670,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
     scale[i] = sv[((int64_t)s * H + h) * D + cg * 8 + i];
     mean[i] = vmean ? vmean[((int64_t)s * H + h) * D + cg * 8 + i] : 0.0f;
   }
-#pragma unroll 2
-  for (int n = n0 + r; n < n1; n += RPP) {
-    H8 x = load_h8_or_zero(src + (int64_t)n * vs.n, 8 * cg < dv);
+  auto codes = [&](const H8& x) {
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = scale[i] > 0.0f ? ((float)x.v[i] - mean[i]) / scale[i] : 0.0f;
@@ -671,7 +678,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
     uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-    *reinterpret_cast<uint2*>(dst + (int64_t)n * v8s.n) = make_uint2(w0, w1);
+    return make_uint2(w0, w1);
+  };
+  if (8 * cg < dv) {  // the channel test stays outside the loop so that the unrolled loads issue together
+#pragma unroll 2
+    for (int n = n0 + r; n < n1; n += RPP)
+      *reinterpret_cast<uint2*>(dst + (int64_t)n * v8s.n) = codes(load_h8(src + (int64_t)n * vs.n));
+  } else {  // padding channels (head_dim 96): the codes of zeros
+    H8 z;
+    *reinterpret_cast<uint4*>(&z) = make_uint4(0u, 0u, 0u, 0u);
+    const uint2 c = codes(z);
+    for (int n = n0 + r; n < n1; n += RPP) *reinterpret_cast<uint2*>(dst + (int64_t)n * v8s.n) = c;
   }
 }
 
@@ -700,12 +717,18 @@ __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restr
   const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
   double acc[8] = {};
   Extremes ex;
+  if (8 * cg < dv) {  // the channel test stays outside the loop so that the unrolled loads issue together
 #pragma unroll 4
-  for (int n = n0 + r; n < n1; n += RPP) {
-    const H8 x = load_h8_or_zero(base + (int64_t)n * vs.n, 8 * cg < dv);
-    ex.add(x);
+    for (int n = n0 + r; n < n1; n += RPP) {
+      const H8 x = load_h8(base + (int64_t)n * vs.n);
+      ex.add(x);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+      for (int i = 0; i < 8; ++i) acc[i] += (double)(float)x.v[i];
+    }
+  } else if (n0 + r < n1) {  // padding channels (head_dim 96): sums 0, maximum and minimum 0
+    H8 z;
+    *reinterpret_cast<uint4*>(&z) = make_uint4(0u, 0u, 0u, 0u);
+    ex.add(z);
   }
   __shared__ double rsum[RPP][D];
   __shared__ float rmax[RPP][D], rmin[RPP][D];
