@@ -12,7 +12,7 @@
 //
 // All of these are HBM-bound streaming passes.  Rounding is fixed so that the
 // results are bit-exact against a plain CPU implementation:
-//   * K column sums are taken in fp64 (one partial per Q block, fused with
+//   * K column sums are taken in fp64 (one partial per chunk of tokens, fused with
 //     the Q quantisation, then a small reduction); every fp16 value is a
 //     multiple of 2^-24 and the sums stay far below 2^29, so each partial sum
 //     is exact and the result is independent of the reduction order.  mean =
@@ -218,26 +218,42 @@ __device__ __forceinline__ float quant_block(const _Float16* __restrict__ src, i
   return scale;
 }
 
-// Exact fp64 column sums of rows [n0, n1) (n1 - n0 <= kKSumRows) of one
+// Exact fp64 column sums of rows [n0, n1) (n1 - n0 <= 128 * NSB) of one
 // (sequence, head): thread (r, cg) adds rows n0 + r + RPP*j of channels 8cg ..
 // 8cg+7 (base points at channel 8cg of token 0), then the RPP partials of a
 // channel are added in LDS and written to out[0 .. D-1].  Every fp16 value is a
 // multiple of 2^-24 and |sum| < 2^29, so the sums are exact in any order.
-template <int D>
+template <int D, int NSB = 1>
 __device__ __forceinline__ void colsum_chunk(const _Float16* __restrict__ base, int64_t sn, int n0, int n1, bool cgv,
                                              double* __restrict__ out) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   double acc[8] = {};
-  static_assert(kKSumRows <= 128, "a chunk fits the register-cached rows");
   {
-    BlockRows<D> rows;
-    rows.load(base, sn, n0, n1, cgv);
+    // up to NSB blocks of 128 rows; the next block's loads are in flight while a
+    // block is added (a block wholly past n1 re-reads row n1 - 1 and adds nothing)
+    auto add = [&](const BlockRows<D>& rows, int sb) {
 #pragma unroll
-    for (int j = 0; j < BlockRows<D>::R; ++j)
-      if (n0 + r + RPP * j < n1)
+      for (int j = 0; j < BlockRows<D>::R; ++j)
+        if (n0 + 128 * sb + r + RPP * j < n1)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += (double)(float)rows.x[j].v[i];
+          for (int i = 0; i < 8; ++i) acc[i] += (double)(float)rows.x[j].v[i];
+    };
+    auto blk = [&](int sb) { return min(n0 + 128 * sb, n1 - 1); };
+    BlockRows<D> ra, rb;
+    ra.load(base, sn, n0, n1, cgv);
+    if constexpr (NSB == 1) {
+      add(ra, 0);
+    } else {
+      static_assert(NSB % 2 == 0, "blocks go in pairs");
+#pragma unroll 1
+      for (int sb = 0; sb < NSB; sb += 2) {
+        rb.load(base, sn, blk(sb + 1), n1, cgv);
+        add(ra, sb);
+        if (sb + 2 < NSB) ra.load(base, sn, blk(sb + 2), n1, cgv);
+        add(rb, sb + 1);
+      }
+    }
   }
   __shared__ double red[RPP][D];
 #pragma unroll
@@ -255,7 +271,7 @@ __device__ __forceinline__ void colsum_chunk(const _Float16* __restrict__ base, 
 // (INT8 Q' = Q * sm_scale): block x of blk_q rows, or for blk_q == 1 (one
 // scale per token) the RPP rows x*RPP .. x*RPP+RPP-1, TPR threads per row.
 // Workgroups x >= nqw with a K head (y < kv_heads) take the fp64 column sums
-// of K over the tokens of chunk x - nqw (kKSumRows tokens), one partial per
+// of K over the tokens of chunk x - nqw (kKChunkRows tokens), one partial per
 // chunk.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
@@ -306,10 +322,10 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
   if (h >= kv_heads) return;
   const int64_t skv = (int64_t)s * kv_heads + h;
   const int ci = x - nqw;
-  const int n0 = ci * kKSumRows;
+  const int n0 = ci * kKChunkRows;
   if (n0 >= L) return;
-  colsum_chunk<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, min(L, n0 + kKSumRows), cgv,
-                  part + (skv * nks + ci) * D);
+  colsum_chunk<D, kKChunkRows / 128>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, min(L, n0 + kKChunkRows),
+                                     cgv, part + (skv * nks + ci) * D);
 }
 
 // grid (nks, heads, nseq), kQThreads (heads: of Q).  Smooth Q: the fp64 column sums of
@@ -368,10 +384,11 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
                                                              const int32_t* __restrict__ cu, int max_seqlen,
-                                                             int nks, double scale, float* __restrict__ km) {
+                                                             int nks, int chunk, double scale,
+                                                             float* __restrict__ km) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
   const int L = seq_len(cu, s, max_seqlen);
-  const int nb = (L + kKSumRows - 1) / kKSumRows;
+  const int nb = (L + chunk - 1) / chunk;
   const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nks * D + c, nb, c, g);
   if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)((sum / (double)L) * scale) : 0.0f;
 }
@@ -492,7 +509,8 @@ __global__ __launch_bounds__(kQThreads) void k_q_delta(const _Float16* __restric
 template <int D, bool FOLD>
 __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
                                                        const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
-                                                       int nbk, int nks, int dv, const double* __restrict__ part,
+                                                       int nbk, int nks, int chunk, int dv,
+                                                       const double* __restrict__ part,
                                                        float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
                                                        float* __restrict__ sk) {
   constexpr int TPR = D / 8;
@@ -512,7 +530,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
   if constexpr (FOLD) {
     __shared__ float kmean[D];
     const int c = threadIdx.x % D, g = threadIdx.x / D;
-    const double sum = sum_partials<D>(part + sh * nks * D + c, (L + kKSumRows - 1) / kKSumRows, c, g);
+    const double sum = sum_partials<D>(part + sh * nks * D + c, (L + chunk - 1) / chunk, c, g);
     if (g == 0) {
       const float mv = (float)(sum / (double)L);
       kmean[c] = mv;
@@ -803,35 +821,39 @@ __global__ __launch_bounds__(D) void k_v_finalize(const double* __restrict__ psu
 
 // Heads with at most this many K column-sum partials fold the mean into k_quant_k.
 constexpr int kFoldMaxBlocks = 64;
+// Sequences up to this many tokens fold the K mean into k_quant_k (each of its workgroups
+// adds at most 64 partials of kKSumRows tokens, or 16 of kKChunkRows).
+constexpr int kFoldMaxTokens = kFoldMaxBlocks * kKSumRows;
 
 hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st) {
   SAGE_DISPATCH_D(p.head_dim, {
     constexpr int RPP = kQThreads / (D / 8);  // rows per workgroup of the per-token path
     const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
-    hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st,
+    const int nkc = (p.max_seqlen + kKChunkRows - 1) / kKChunkRows;  // K column-sum chunks per head
+    hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + nkc, p.heads, p.nseq), dim3(kQThreads), 0, st,
                        (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.nbq, nqw,
                        p.nks, p.kv_heads, p.dv, sm_scale, q8, q8s, q_scale, partial);
   });
   return hipGetLastError();
 }
 
-hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
-                          Str k8s, float* k_scale, hipStream_t st) {
+hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, int chunk, float* k_mean,
+                          int8_t* k8, Str k8s, float* k_scale, hipStream_t st) {
   dim3 grid(p.nbk, p.kv_heads, p.nseq);
-  if (p.nks <= kFoldMaxBlocks) {
+  if (p.max_seqlen <= kFoldMaxTokens) {
     SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
                                                    (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
-                                                   p.dv, partial, k_mean, k8, k8s, k_scale));
+                                                   chunk, p.dv, partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
-                                                 partial, p.cu, p.max_seqlen, p.nks, 1.0, k_mean));
+                                                 partial, p.cu, p.max_seqlen, p.nks, chunk, 1.0, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
                                                  (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
-                                                 p.dv, partial, k_mean, k8, k8s, k_scale));
+                                                 chunk, p.dv, partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
 }
 
@@ -852,7 +874,7 @@ hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const 
                          p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
     } else {
       hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
-                         p.max_seqlen, p.nks, (double)sm_scale, q_mean);
+                         p.max_seqlen, p.nks, kKSumRows, (double)sm_scale, q_mean);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hipLaunchKernelGGL((k_quant_q_smooth<D, false>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
                          p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
@@ -873,11 +895,11 @@ hipError_t launch_quant_mxfp4(const Problem& p, const void* Q, Str qs, const voi
                        p.smooth_q ? qpart : nullptr, kpart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st, kpart, p.cu,
-                       p.max_seqlen, p.nks, 1.0, k_mean);
+                       p.max_seqlen, p.nks, kKSumRows, 1.0, k_mean);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.smooth_q) {
       hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
-                         p.max_seqlen, p.nks, (double)sm_scale, q_mean);
+                         p.max_seqlen, p.nks, kKSumRows, (double)sm_scale, q_mean);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL((k_quant_mxfp4<D, true>), dim3(nx, p.heads, p.nseq), dim3(kQThreads), 0, st,

@@ -265,7 +265,7 @@ int run_quantize_smooth_q(const sage_problem* p, const void* Q, sage_strides qs,
   if ((e = sage::launch_quant_q_smooth(q, Q, S(qs), K, S(ks), sm_scale, q8, S(q8s), q_scale, q_mean, qpart, kpart,
                                        st)) != hipSuccess)
     return hip_fail(e, "smooth-Q quantisation launch");
-  if ((e = sage::launch_quant_k(q, K, S(ks), kpart, k_mean, k8, S(k8s), k_scale, st)) != hipSuccess)
+  if ((e = sage::launch_quant_k(q, K, S(ks), kpart, sage::kKSumRows, k_mean, k8, S(k8s), k_scale, st)) != hipSuccess)
     return hip_fail(e, "quant_k launch");
   if ((e = sage::launch_q_delta(q, K, S(ks), q_mean, k_mean, q_delta, S(qds), st)) != hipSuccess)
     return hip_fail(e, "q_delta launch");
@@ -281,7 +281,8 @@ int run_quantize(const sage_problem* p, const void* Q, sage_strides qs, const vo
   if ((e = sage::launch_quant_q_colsum(q, Q, S(qs), K, S(ks), sm_scale, q8, S(q8s), q_scale, colsum, st)) !=
       hipSuccess)
     return hip_fail(e, "quant_q_colsum launch");
-  if ((e = sage::launch_quant_k(q, K, S(ks), colsum, k_mean, k8, S(k8s), k_scale, st)) != hipSuccess)
+  if ((e = sage::launch_quant_k(q, K, S(ks), colsum, sage::kKChunkRows, k_mean, k8, S(k8s), k_scale, st)) !=
+      hipSuccess)
     return hip_fail(e, "quant_k launch");
   return SAGE_OK;
 }

@@ -15,8 +15,12 @@ struct Str {
 
 // Tokens per partial of the V column statistics.
 constexpr int kColChunk = 512;
-// Tokens per partial of the K column sums.
+// Tokens per partial of the K (and Q) column sums; the workspace holds ceil(max_seqlen /
+// kKSumRows) partials per (sequence, head).
 constexpr int kKSumRows = 128;
+// Tokens per partial of the K column sums in the INT8 pre-pass (sage_quantize, sage_attn):
+// fewer partials for the K quantisation to add up.
+constexpr int kKChunkRows = 512;
 
 __device__ __forceinline__ int seq_len(const int32_t* cu, int s, int max_seqlen) {
   return cu ? (cu[s + 1] - cu[s]) : max_seqlen;
@@ -41,11 +45,13 @@ struct Problem {
 
 // ---- pre-pass (prepass.hip) ----
 // INT8 Q blocks (blk_q == 1: one scale per token), plus fp64 column sums of K over chunks of
-// kKSumRows tokens (partial: nseq*kv_heads*nks*head_dim).
+// kKChunkRows tokens (partial: room for nseq*kv_heads*nks*head_dim).
 hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const void* K, Str ks, float sm_scale,
                                  int8_t* q8, Str q8s, float* q_scale, double* partial, hipStream_t st);
-// k_mean = fp32(sum of the partials / L) per (sequence, head, channel), and INT8 K blocks of K - k_mean.
-hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, float* k_mean, int8_t* k8,
+// k_mean = fp32(sum of the partials / L) per (sequence, head, channel), and INT8 K blocks of K - k_mean;
+// the partials cover `chunk` tokens each (kKChunkRows after launch_quant_q_colsum, kKSumRows after
+// launch_quant_q_smooth).
+hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double* partial, int chunk, float* k_mean, int8_t* k8,
                           Str k8s, float* k_scale, hipStream_t st);
 // Smooth Q: fp64 column sums of Q (qpart: nseq*heads*nks*head_dim) and of K (kpart, as
 // launch_quant_q_colsum's partial), q_mean = fp32((sum / L) * sm_scale) per (sequence, query
