@@ -6,10 +6,13 @@ causal: smooth K + INT8 Q/K (sage_quantize), then the fused attention kernel
 (sage_attn_quantized).  Inputs are synthetic (seeded, fp16, already resident
 in HBM before the timed region starts).
 
-value = attention TOPS of the step = (4 B H N^2 d + 4 B H N^2 d / 2) / t.
+value = attention TOPS of the step = (4 B H N^2 d + 4 B H N^2 d / 2) / t,
+with t from K steps that carry no events of their own (an event pair between
+two kernels costs several microseconds on the stream).
 roofline = the dominant kernel (the non-causal fused attention) against the
 MI355X dense INT8 MFMA peak; its duration is measured live with HIP events
-on the stream it runs on.  cpu_baseline = the CPU oracle on the same step.
+around it, on the stream it runs on, in a second pass of the same K steps
+(the pre-pass in a third).  cpu_baseline = the CPU oracle on the same step.
 timing = median and min of the per-launch HIP event times (fused kernel,
 non-causal and causal), the sage_quantize pre-pass against the HBM peak
 (algorithmic bytes: fp16 Q and K read once, int8 written, scales, mean), and
@@ -125,19 +128,21 @@ def main():
     ev = {c: [evpair() for _ in range(args.steps)] for c in (False, True)}
     evq = {c: [evpair() for _ in range(args.steps)] for c in (False, True)}
 
-    def step(i=None, quant_events=False):
-        # timed steps carry events around the fused kernel only; the pre-pass
-        # is timed in a separate pass of the same steps
+    def step(i=None, events=None):
+        # The steps of the timed region carry no events of their own (an event
+        # pair between two kernels costs several microseconds on the stream);
+        # two further passes of the same steps put HIP events around the fused
+        # kernel (events="attn") and around the pre-pass (events="quant").
         for causal in (False, True):
-            if quant_events:
+            if events == "quant":
                 evq[causal][i][0].record(stream)
             quantize()
-            if quant_events:
+            if events == "quant":
                 evq[causal][i][1].record(stream)
-            elif i is not None:
+            if events == "attn":
                 ev[causal][i][0].record(stream)
             attention(causal)
-            if i is not None and not quant_events:
+            if events == "attn":
                 ev[causal][i][1].record(stream)
 
     if args.copy_calib:
@@ -156,9 +161,10 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    for i in range(args.steps):
-        step(i, quant_events=True)
-    torch.cuda.synchronize()
+    for events in ("attn", "quant"):
+        for i in range(args.steps):
+            step(i, events)
+        torch.cuda.synchronize()
     ms_step = total_ms / args.steps
     ops_nc = sage.attention_ops([N] * B, H, d, False)
     ops_c = sage.attention_ops([N] * B, H, d, True)
