@@ -533,15 +533,35 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       };
       // four independent max3 chains (one wave does all the VALU work of a
       // phase, so a single chain would leave the VALU waiting on its latency)
-      float mc[4];
+      float mx;
+      if constexpr (!NEGX) {
+        // every x is a positive float, or 0 for a masked key, so its bits order
+        // as integers: v_max3_i32 on the raw sums, with none of the
+        // canonicalising v_max_f32 that a float maximum of them costs
+        auto xi = [&](int jt, int r) {
+          if constexpr (MASKED) return valid[jt][r] ? sc[jt][r] : 0;
+          return sc[jt][r];
+        };
+        int mc[4];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) mc[c4] = fmaxf(xv(c4 >> 1, 8 * (c4 & 1)), xv(c4 >> 1, 8 * (c4 & 1) + 1));
+        for (int c4 = 0; c4 < 4; ++c4) mc[c4] = max(xi(c4 >> 1, 8 * (c4 & 1)), xi(c4 >> 1, 8 * (c4 & 1) + 1));
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
+        for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-        for (int r = 2; r < 8; r += 2)
-          mc[c4] = fmaxf(fmaxf(mc[c4], xv(c4 >> 1, 8 * (c4 & 1) + r)), xv(c4 >> 1, 8 * (c4 & 1) + r + 1));
-      float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+          for (int r = 2; r < 8; r += 2)
+            mc[c4] = max(max(mc[c4], xi(c4 >> 1, 8 * (c4 & 1) + r)), xi(c4 >> 1, 8 * (c4 & 1) + r + 1));
+        mx = __int_as_float(max(max(mc[0], mc[1]), max(mc[2], mc[3])));
+      } else {
+        float mc[4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) mc[c4] = fmaxf(xv(c4 >> 1, 8 * (c4 & 1)), xv(c4 >> 1, 8 * (c4 & 1) + 1));
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+          for (int r = 2; r < 8; r += 2)
+            mc[c4] = fmaxf(fmaxf(mc[c4], xv(c4 >> 1, 8 * (c4 & 1) + r)), xv(c4 >> 1, 8 * (c4 & 1) + r + 1));
+        mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
+      }
       mx = xhalf_max(mx);
       // every real x is >= 1.5*2^23 - 2^21 > 0, so 0 means "all masked": leave m alone
       // (smooth Q: a masked x is -inf, and so is mt)
