@@ -12,17 +12,21 @@ two kernels costs several microseconds on the stream).
 roofline = the dominant kernel (the non-causal fused attention) against the
 MI355X dense INT8 MFMA peak; its duration is measured live with HIP events
 around it, on the stream it runs on, in a second pass of the same K steps
-(the pre-pass in a third).  cpu_baseline = the CPU oracle on the same step.
+(the pre-pass in a third).  cpu_baseline = the CPU oracle on the same step,
+its (head, mask) units spread over one single-threaded worker process per
+host core.
 timing = median and min of the per-launch HIP event times (fused kernel,
 non-causal and causal), the sage_quantize pre-pass against the HBM peak
 (algorithmic bytes: fp16 Q and K read once, int8 written, scales, mean), and
 sage_attn end to end (its own workspace).  inputs_sha256 = provenance of
 the synthetic fp16 Q, K, V.
-extra = kernel-only TOPS of the fused kernel on the larger workloads, and
-sage_attn end to end (pre-pass included) plain, with Q smoothed, and with 4-bit
-(MXFP4) Q and K on one.
+extra = the larger workloads, inputs drawn with each workload's own recipe
+(synth.generate): kernel-only TOPS of the fused kernel, sage_attn end to end
+(pre-pass included) plain, with Q smoothed and with 4-bit (MXFP4) Q and K,
+and the pre-pass alone at N=32K; median and min over 50 timed calls each.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --profile CASE [--steps K] [--warmup W]   (one extra case only)
 """
 from __future__ import annotations
 
@@ -52,6 +56,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="first run a plain copy kernel of 256 MiB in / 256 MiB out (HBM counter calibration)")
+    ap.add_argument("--profile", metavar="CASE",
+                    help="run only this extra case (--warmup, then --steps timed calls) and print its timing: "
+                         "the command the rocprofv3 summaries are taken with")
     return ap.parse_args()
 
 
@@ -93,6 +100,15 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     L = sage.lib()
+    if args.copy_calib:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)         # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del src, dst
+    if args.profile:
+        profile_case(sage, torch, dev, args.profile, args.steps, args.warmup)
+        return
 
     wl = synth.TEXT
     inp = synth.generate(wl)
@@ -145,12 +161,6 @@ def main():
             if events == "attn":
                 ev[causal][i][1].record(stream)
 
-    if args.copy_calib:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)         # reads 256 MiB, writes 256 MiB
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -251,109 +261,182 @@ def end_to_end(sage, torch, q, k, v, wl, ops_nc, ops_c, warmup=10, runs=50):
     return res
 
 
-def extra_workloads(sage, torch, dev):
-    """Kernel-only TOPS of the fused attention on the larger workloads
-    (inputs drawn on the GPU with the workloads' distributions)."""
-    from quantized_attention_transformer_amd import synth
-    res = {}
-    g = torch.Generator(device=dev)
-    cases = [("long causal B1 H32 N32768 d128", synth.LONG, True, 0, None),
-             ("fp8-PV B4 H16 N8192 d128", synth.FP8, False, 1, None),
-             ("fp8-PV smooth-V B4 H16 N8192 d128", synth.FP8, False, 2, None),
-             ("fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, None),
-             ("video B2 H24 N16384 d64", synth.VIDEO, False, 0, None),
-             ("varlen causal H32 d128", synth.VARLEN, True, 0, "varlen"),
-             ("gqa causal B1 H32 kv8 N8192 d128", synth.LONG, True, 0, "gqa"),
-             # whole forward pass (sage_attn: pre-pass + fused kernel), plain and with Q smoothed
-             ("sage_attn fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "e2e"),
-             ("sage_attn smooth-Q fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "sq"),
-             ("sage_attn 4-bit QK (MXFP4) fp16-PV B4 H16 N8192 d128", synth.FP8, False, 0, "fp4"),
-             ("sage_attn 4-bit QK (MXFP4) FP8-PV B4 H16 N8192 d128", synth.FP8, False, 1, "fp4")]
-    for name, wl, causal, mode, kind in cases:
-        g.manual_seed(wl.seed)
-        if kind == "varlen":
-            import numpy as np
-            lens = synth.draw_varlen_lengths(np.random.default_rng(wl.seed), wl.varlen_nseq, wl.varlen_min,
-                                             wl.varlen_max, wl.varlen_total_max)
-            T = int(lens.sum())
-            shape = (T, wl.heads, wl.head_dim)
-            cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=dev)
-            kw = dict(cu_seqlens=cu, max_seqlen=int(lens.max()))
-            seqlens = lens.tolist()
-        elif kind == "gqa":
-            shape = (1, 8192, wl.heads, wl.head_dim)
-            kw = {}
-            seqlens = [8192]
-        else:
-            shape = (wl.batch, wl.seqlen, wl.heads, wl.head_dim)
-            kw = {}
-            seqlens = [wl.seqlen] * wl.batch
-        q = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
-        bias = torch.randn((wl.heads, wl.head_dim), generator=g, device=dev) * wl.bias_std
-        k = (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) + bias).half()
-        v = torch.randn(shape, generator=g, device=dev, dtype=torch.float32).half()
-        if kind == "gqa":                         # 8 K/V heads for the 32 query heads
-            k, v = k[:, :, :8].contiguous(), v[:, :, :8].contiguous()
-        qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
-        vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
-        out = torch.empty_like(q)
-        ws = None
-        if kind in ("e2e", "sq", "fp4"):
-            prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k)
-            prob.smooth_q = int(kind == "sq")
-            prob.qk_fp4 = int(kind == "fp4")
-            ws = torch.empty(sage.workspace_bytes(prob, mode), dtype=torch.uint8, device=dev)
+# Extra workloads: (name, workload, causal, pv_mode, kind).  kind "kernel" times
+# the fused kernel alone (sage_attn_quantized on pre-quantised inputs), "e2e"
+# sage_attn (pre-pass + fused kernel), "sq" / "fp4" sage_attn with Q smoothed /
+# with 4-bit (MXFP4) Q and K, "prepass" sage_quantize alone, "gqa" the fused
+# kernel with 8 K/V heads for the 32 query heads.
+EXTRA_CASES = [
+    ("long causal B1 H32 N32768 d128", "LONG", True, 0, "kernel"),
+    ("fp8-PV B4 H16 N8192 d128", "FP8", False, 1, "kernel"),
+    ("fp8-PV smooth-V B4 H16 N8192 d128", "FP8", False, 2, "kernel"),
+    ("fp16-PV B4 H16 N8192 d128", "FP8", False, 0, "kernel"),
+    ("video B2 H24 N16384 d64", "VIDEO", False, 0, "kernel"),
+    ("varlen causal H32 d128", "VARLEN", True, 0, "kernel"),
+    ("gqa causal B1 H32 kv8 N8192 d128", "LONG", True, 0, "gqa"),
+    ("sage_attn fp16-PV B4 H16 N8192 d128", "FP8", False, 0, "e2e"),
+    ("sage_attn FP8-PV B4 H16 N8192 d128", "FP8", False, 1, "e2e"),
+    ("sage_attn smooth-Q fp16-PV B4 H16 N8192 d128", "FP8", False, 0, "sq"),
+    ("sage_attn 4-bit QK (MXFP4) fp16-PV B4 H16 N8192 d128", "FP8", False, 0, "fp4"),
+    ("sage_attn 4-bit QK (MXFP4) FP8-PV B4 H16 N8192 d128", "FP8", False, 1, "fp4"),
+    ("sage_quantize long B1 H32 N32768 d128", "LONG", False, 0, "prepass"),
+]
+
+
+class _Inputs:
+    """Device copies of one workload's seeded inputs (synth.generate, the
+    workload's own recipe), drawn once and shared by the cases that use it."""
+
+    def __init__(self, torch, dev):
+        self.torch, self.dev, self.cache = torch, dev, {}
+
+    def get(self, wl_name, gqa=False):
+        from quantized_attention_transformer_amd import synth
+        key = (wl_name, gqa)
+        if key not in self.cache:
+            self.cache.clear()
+            self.torch.cuda.empty_cache()
+            wl = getattr(synth, wl_name)
+            inp = synth.generate(wl, seqlen=8192) if gqa else synth.generate(wl)
+            t = [self.torch.from_numpy(x).to(self.dev) for x in (inp.q, inp.k, inp.v)]
+            if gqa:                           # 8 K/V heads for the 32 query heads
+                t[1], t[2] = t[1][:, :, :8].contiguous(), t[2][:, :, :8].contiguous()
+            cu = None if inp.cu_seqlens is None else self.torch.from_numpy(inp.cu_seqlens).to(self.dev)
+            self.cache[key] = (wl, t, cu, inp.seqlens.tolist())
+            del inp
+        return self.cache[key]
+
+
+def prepare_case(sage, torch, inputs, name, wl_name, causal, mode, kind):
+    """Returns (run, ops, bytes): a closure that enqueues one call of the case,
+    its attention operation count (0 for the pre-pass) and, for the pre-pass,
+    its algorithmic HBM bytes."""
+    wl, (q, k, v), cu, seqlens = inputs.get(wl_name, gqa=(kind == "gqa"))
+    kw = {} if cu is None else dict(cu_seqlens=cu, max_seqlen=max(seqlens))
+    H, d = q.shape[-2], q.shape[-1]
+    if kind == "prepass":
+        prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k, **kw)
+        ws = torch.empty(max(16, sage.quantize_workspace_bytes(prob)), dtype=torch.uint8, device=q.device)
 
         def run():
-            if ws is not None:
-                sage.attn(q, k, v, causal=causal, pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out,
-                          workspace=ws, smooth_q=(kind == "sq"), qk_fp4=(kind == "fp4"))
-                return
+            sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, workspace=ws, **kw)
+        ntok = sum(seqlens)
+        nbq = sum(-(-L // wl.blk_q) for L in seqlens)
+        nbk = sum(-(-L // wl.blk_k) for L in seqlens)
+        nbytes = 3 * 2 * ntok * H * d + 4 * H * (nbq + nbk) + 4 * len(seqlens) * H * d
+        return run, 0.0, nbytes
+    out = torch.empty_like(q)
+    if kind in ("e2e", "sq", "fp4"):
+        prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k, **kw)
+        prob.smooth_q = int(kind == "sq")
+        prob.qk_fp4 = int(kind == "fp4")
+        ws = torch.empty(sage.workspace_bytes(prob, mode), dtype=torch.uint8, device=q.device)
+
+        def run():
+            sage.attn(q, k, v, causal=causal, pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out,
+                      workspace=ws, smooth_q=(kind == "sq"), qk_fp4=(kind == "fp4"), **kw)
+    else:
+        qd = sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, **kw)
+        vv, sv = (sage.quantize_v_fp8(v, smooth=(mode == 2), **kw) if mode >= 1 else (v, None))
+
+        def run():
             sage.attn_quantized(qd["q8"], qd["k8"], qd["q_scale"], qd["k_scale"], vv, v_scale=sv, causal=causal,
                                 pv_mode=mode, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out, **kw)
-        for _ in range(2):
-            run()
-        torch.cuda.synchronize()
-        n = 5
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    return run, sage.attention_ops(seqlens, H, d, causal), 0
+
+
+def time_case(torch, run, warmup=10, runs=50):
+    """Per-call HIP event times (ms) of `runs` calls after `warmup` untimed ones."""
+    import numpy as np
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for a, b in evs:
         a.record()
-        for _ in range(n):
-            run()
+        run()
         b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / n
-        ops = sage.attention_ops(seqlens, wl.heads, wl.head_dim, causal)
-        tops = ops / (ms * 1e-3) / 1e12
-        res[name] = {"kernel_ms": round(ms, 4), "TOPS": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
-        del q, k, v, qd, vv, out, ws
-        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def case_result(t, ops, nbytes):
+    import numpy as np
+    med, mn = float(np.median(t)), float(t.min())
+    r = {"runs": int(len(t)), "ms_median": round(med, 5), "ms_min": round(mn, 5)}
+    if ops:
+        r.update(TOPS=round(ops / (med * 1e-3) / 1e12, 1), TOPS_best=round(ops / (mn * 1e-3) / 1e12, 1),
+                 frac_int8_peak=round(ops / (med * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4))
+    if nbytes:
+        r.update(algorithmic_bytes=int(nbytes), GBps=round(nbytes / (med * 1e-3) / 1e9, 1),
+                 frac_hbm_peak=round(nbytes / (med * 1e-3) / HBM_PEAK_BPS, 4))
+    return r
+
+
+def extra_workloads(sage, torch, dev, runs=50):
+    """The larger workloads (inputs drawn with each workload's own recipe):
+    kernel-only TOPS of the fused attention, sage_attn end to end, and the
+    pre-pass at N=32K; median and min over `runs` timed calls each."""
+    inputs = _Inputs(torch, dev)
+    res = {}
+    for name, wl_name, causal, mode, kind in EXTRA_CASES:
+        run, ops, nbytes = prepare_case(sage, torch, inputs, name, wl_name, causal, mode, kind)
+        res[name] = case_result(time_case(torch, run, runs=runs), ops, nbytes)
+        print(f"extra: {name}: {res[name]}", file=sys.stderr, flush=True)
+        del run
+    inputs.cache.clear()
+    torch.cuda.empty_cache()
     return res
+
+
+def profile_case(sage, torch, dev, name, steps, warmup):
+    """Only one extra case, `steps` timed calls (for rocprofv3 runs)."""
+    match = [c for c in EXTRA_CASES if c[0] == name]
+    if not match:
+        raise SystemExit(f"unknown case {name!r}; cases: " + "; ".join(c[0] for c in EXTRA_CASES))
+    run, ops, nbytes = prepare_case(sage, torch, _Inputs(torch, dev), *match[0])
+    r = case_result(time_case(torch, run, warmup=warmup, runs=steps), ops, nbytes)
+    print(json.dumps({"case": name, **r}), flush=True)
+
+
+def _oracle_unit(a):
+    """One (head, mask) unit of the oracle, single-threaded (a worker process)."""
+    q, k, v, seqlens, causal, blk_q, blk_k = a
+    from oracle import sage_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=1)
+    except ImportError:                      # pragma: no cover
+        ctx = None
+    try:
+        O.sage_attn(q, k, v, seqlens, None, causal, blk_q, blk_k)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
 
 
 def cpu_baseline(inp, wl, ops):
     """The CPU oracle (as it stands) on the same step: quantisation and fp64
-    attention, non-causal then causal, full workload."""
-    from oracle import sage_oracle as O
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-    except ImportError:                      # pragma: no cover
-        threadpool_limits, threadpool_info = None, None
-    cores = min(16, len(os.sched_getaffinity(0)))
-    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
-    try:
+    attention, non-causal then causal, full workload.  Every (head, mask) pair
+    is an independent unit (the mean, the scales and the softmax rows are per
+    head), so the units run in parallel worker processes, one per host core
+    the process may use, each single-threaded (its BLAS included)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    affinity = len(os.sched_getaffinity(0))
+    H = inp.q.shape[2]
+    units = [(inp.q[:, :, h:h + 1], inp.k[:, :, h:h + 1], inp.v[:, :, h:h + 1], inp.seqlens, causal,
+              wl.blk_q, wl.blk_k) for causal in (False, True) for h in range(H)]
+    workers = min(affinity, len(units))
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_unit, units[:workers]))      # start the workers (imports) before timing
         t = time.perf_counter()
-        for causal in (False, True):
-            O.sage_attn(inp.q, inp.k, inp.v, inp.seqlens, None, causal, wl.blk_q, wl.blk_k)
+        list(ex.map(_oracle_unit, units))
         dt = time.perf_counter() - t
-        used = cores
-        if threadpool_info:
-            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": used, "kind": "oracle",
+    return {"value": round(ops / dt / 1e12, 5), "unit": "TOPS", "cores": workers, "kind": "oracle",
+            "host_affinity_cores": affinity, "host_nproc": os.cpu_count(),
             "sample": f"the full step (B1 H8 N4096 d128, quantise + attention, non-causal and causal) in "
-                      f"{dt:.1f} s; matrix products on {used} BLAS threads, elementwise work single-threaded"}
+                      f"{dt:.2f} s: {len(units)} (head, mask) units over {workers} single-threaded worker "
+                      f"processes (numpy, BLAS limited to one thread each)"}
 
 
 if __name__ == "__main__":

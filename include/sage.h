@@ -25,8 +25,11 @@
  *   `cu_seqlens`, a DEVICE array of nseq+1 int32 prefix offsets (cu[0] = 0,
  *   non-decreasing, cu[nseq] = total_tokens); sequence s is tokens
  *   [cu[s], cu[s+1]).  `max_seqlen` must be >= every length (the library
- *   never reads cu_seqlens on the host).  Queries and keys are the same
- *   tokens (self-attention).
+ *   never reads cu_seqlens on the host); total_tokens < 2^31.  A cu_seqlens
+ *   that breaks these rules gives wrong results, not out-of-bounds
+ *   accesses: the kernels clamp every offset to [0, total_tokens] and every
+ *   length to max_seqlen.  Queries and keys are the same tokens
+ *   (self-attention).
  * Tensors.  Element strides in a sage_strides {s, h, n}: element (seq s,
  *   head h, token n, channel c) of a dense tensor is at s*S.s + h*S.h +
  *   n*S.n + c; in a packed tensor it is at (cu[s] + n)*S.n + h*S.h + c
@@ -230,10 +233,16 @@ int sage_attn(const sage_problem* p,
               int causal, float sm_scale, int pv_mode,
               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Debug: the INT32 scores of the fused kernel's integer stage, written by
- * the same MFMA code path before dequantisation.  Dense problems only, with
- * max_seqlen <= 1024; s_out is int32 [nseq][heads][max_seqlen][max_seqlen]
- * (query-major), every entry written. */
+/* Debug: the INT32 scores S_int = q8 . k8^T of the fused kernel's integer
+ * stage ("SageAttention：低比特量化Attention，实现推理加速", 技术方案 item 2:
+ * INT8 product, INT32 accumulator), taken from the fused kernel itself: a
+ * dump instantiation of it runs the same K tile ring, the same steady-state
+ * and edge-phase INT8 MFMA code and the same phase schedule, and writes every
+ * tile's sums at the start of its softmax, before dequantisation (V is not
+ * read, no scale is read, no O is written).  Dense problems only, with
+ * max_seqlen <= 1024 and a multiple of 4; q8/k8 as for sage_attn_quantized
+ * (k8 with kv_heads heads); s_out is int32 [nseq][heads][max_seqlen]
+ * [max_seqlen] (query-major), every entry written. */
 int sage_debug_qk_i32(const sage_problem* p,
                       const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,
                       int32_t* s_out, void* stream);

@@ -309,14 +309,23 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4>
+// DUMP (debug, INT8 fp16-path only): the same kernel writes each tile's raw
+// INT32 scores to a.dump at the start of its softmax -- after the steady-state
+// (qk_pv) or edge-phase (qk_tile) matrix phase that produced them, through the
+// same K ring -- and stores no O; V is not read (empty descriptors) and no
+// scale is loaded (the softmax runs on scale 1, its result unused).
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4, bool DUMP = false>
 __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, lds_u8* const lds) {
+  static_assert(!DUMP || (!FP8 && !CAUSAL && KSU && !SQ && !QK4), "dump: the plain INT8 kernel");
   using S = Lds<D, FP8, QK4>;
   static_assert(!SQ || KSU, "smooth Q needs key blocks that are multiples of the tile");
   static_assert(!QK4 || (D == 128 && KSU), "4-bit Q.K^T: head_dim 128, no per-block k-scale table");
-  // 4-bit Q.K^T: the MFMA returns S itself (fp32); INT8: the float 1.5*2^23 + S
-  constexpr float MAG = QK4 ? 0.0f : kMagic;
+  // The softmax's score x: INT8 without smooth Q, the float 1.5*2^23 + S read
+  // straight from the MFMA; smooth Q, S + delta/(qs ks) (the seed subtracted
+  // exactly first); 4-bit, S itself (fp32 from the MFMA).
+  constexpr float MAG = (QK4 || SQ) ? 0.0f : kMagic;
   constexpr bool NEGX = SQ || QK4;  // scores may be <= 0: a masked key is -inf
+  constexpr bool BIASED = KSU && !NEGX;  // x carries the seed into the exponent's FMA
   // Smooth Q: a zero block scale (all codes 0) is replaced.  x' = x + delta /
   // (qs ks) is rounded to fp32, so the unit qs ks must not be coarse next to
   // delta: a zero Q scale becomes 2^-40 (x' then holds delta at fp32 relative
@@ -341,16 +350,16 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int64_t sh = (int64_t)s * p.heads + h;  // (sequence, query head)
   const int64_t skv = kvg;                       // (sequence, K/V head)
 
-  const int L = seq_len(p.cu, s, p.max_seqlen);
+  const int L = seq_len(p.cu, s, p.max_seqlen, p.total);
   const int q0 = qt * BM;
   if (q0 >= L) return;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = w >> 2;  // half: key tiles t = hf (mod 2)
 
-  const int8_t* __restrict__ qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h);
-  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, kvh);
-  const uint8_t* vseq = (const uint8_t*)a.v + seq_head_base(p.cu, a.vs, s, kvh) * (FP8 ? 1 : 2);
+  const int8_t* __restrict__ qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h, p.total);
+  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, kvh, p.total);
+  const uint8_t* vseq = (const uint8_t*)a.v + seq_head_base(p.cu, a.vs, s, kvh, p.total) * (FP8 ? 1 : 2);
   const int64_t kn = a.k8s.n, vn = a.vs.n * (FP8 ? 1 : 2);  // row strides in bytes
   const float* __restrict__ ksc = a.k_scale + skv * p.nbk;
   const __attribute__((address_space(4))) float* ksc_c = (const __attribute__((address_space(4))) float*)ksc;
@@ -374,13 +383,13 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk)
         qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
-      wq = *reinterpret_cast<const uint32_t*>(a.qsc4 + seq_head_base(p.cu, a.qss4, s, h) + (int64_t)i * a.qss4.n);
+      wq = *reinterpret_cast<const uint32_t*>(a.qsc4 + seq_head_base(p.cu, a.qss4, s, h, p.total) + (int64_t)i * a.qss4.n);
     }
   } else if (i < L) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       qf[kk] = *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g);
-    qraw = a.q_scale[sh * p.nbq + i / p.blk_q];
+    qraw = DUMP ? 1.0f : a.q_scale[sh * p.nbq + i / p.blk_q];
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = v4i{0, 0, 0, 0};
@@ -408,7 +417,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     vaddr[ct] = vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
   }
 
-  const bool ks_in_lds = KSU && !QK4 && ntiles <= S::KSCAP;
+  const bool ks_in_lds = KSU && !QK4 && !DUMP && ntiles <= S::KSCAP;
 
   DmaPlan<D, FP8, QK4> dma;
   dma.init(w & 3, lane, kn, vn);  // the plan covers a tile with the 4 waves of one half
@@ -425,7 +434,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   for (int ct = 0; ct < D / 32; ++ct) o[ct] = v16f{};
   v16i sc[2];   // S of the tile between its matrix and vector phases
   v8h pf[4];    // fp16 P (between the vector phase and the next matrix phase)
-  v8i pf8;      // E4M3 P
+  v8i pf8 = {};  // E4M3 P
 
   // O^T += V^T . P^T for the tile at LDS byte offset vso
   auto pv = [&](uint32_t vso) {
@@ -471,9 +480,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // one value per tile, from the LDS table (longer sequences: a scalar
       // load, counted by lgkmcnt rather than by the tile loads' vmcnt); 4-bit:
       // the scales are inside S
-      const float v = QK4 ? qsc
-                          : qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
-                                             : keff(ksc_c[min(j0, L - 1) / p.blk_k]));
+      float v = (QK4 || DUMP) ? qsc
+                              : qsc * (ks_in_lds ? *(const LDS float*)(lds + S::KSTAB + 4 * t)
+                                                 : keff(ksc_c[min(j0, L - 1) / p.blk_k]));
+      // 22 significant bits: 1.5*2^23 * c is then exact in fp32 (3 times a
+      // 22-bit integer fits 24 bits), which the exponent's FMA relies on
+      if constexpr (!QK4) v = __uint_as_float((__float_as_uint(v) + 2u) & ~3u);
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -497,7 +509,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j0 = t * BN;
     const auto& c = ck.c;
-    // smooth Q: x' = x + delta_j / (qs ks), in place of the raw scores
+    // smooth Q: x' = S + delta_j / (qs ks), in place of the raw scores.  The
+    // INT8 seed goes first (exact: S is an integer below 2^22), so the sum is
+    // rounded at the size of the score, not of 1.5*2^23 (4-bit: S has none).
     if constexpr (SQ) {
       const float f = __builtin_amdgcn_rcpf(c[0][0]) * kLog2e;
       const lds_u8* dl = lds + dslot + 16 * g;
@@ -508,7 +522,8 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
           const v4f d4 = *(const LDS v4f*)(dl + 4 * (32 * jt + 8 * q));
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sc[jt][4 * q + e] = __float_as_int(__builtin_fmaf(d4[e], f, __int_as_float(sc[jt][4 * q + e])));
+            sc[jt][4 * q + e] = __float_as_int(
+                __builtin_fmaf(d4[e], f, __int_as_float(sc[jt][4 * q + e]) - (QK4 ? 0.0f : kMagic)));
         }
     }
     bool valid[2][16];
@@ -594,7 +609,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // lazy running maximum: a row moves its reference m only when the tile
       // maximum exceeds it by more than 8 (P <= 2^8 stays exact in fp16 and
       // far from overflow)
-      const float mn = mt > m + 8.0f ? mt : m;
+      // (kept an integer: with c below 1 the bias below is then exact, and
+      // every rescale factor 2^(m_old - m_new) is a power of two)
+      const float mn = mt > m + 8.0f ? ceilf(mt) : m;
       alpha = mn == m ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
       m = mn;
     }
@@ -604,9 +621,33 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
     }
     const float mref = FP8 ? m - kLog2_448 : m;  // FP8: P scaled by 448 inside the exponent
-    const float bias = __builtin_fmaf(MAG, c[0][0], mref);
-    auto prob = [&](int jt, int r) {
-      float arg = KSU ? __builtin_fmaf(__int_as_float(sc[jt][r]), c[0][0], -bias) : y[jt][r] - mref;
+    // Exponent x c - (MAG c + mref), one FMA per score.  The FMA rounds once,
+    // at the size of the result; what remains is the rounding of the bias
+    // MAG c + mref, the same for every key of the tile but not from tile to
+    // tile.  fp16 P.V: c has 22 significant bits, so MAG c = 3 * 2^22 * c is
+    // an exact multiple of twice c's last bit, and m is an integer; while c <
+    // 1 that unit divides m too and the sum stays below 2^24 of them (|m| <=
+    // 2^21 c + 9), so the bias is exact (for c below 2^-18, where m is the
+    // larger term, it is rounded at the size of m only).  FP8: mref = m -
+    // log2(448) is not an
+    // integer; the bias is rounded up (by at least its rounding error), so
+    // 448 P never exceeds 448, and its error, at most an ulp of MAG c, stays
+    // below 2^-10 log2 units while c < 2^-9 (scores of unit-scale Q and K
+    // have c ~ 2^-12).  Larger c (any lane) take the slow form: the seed
+    // subtracted first, exactly, one more instruction per score.
+    bool slow = false;
+    if constexpr (BIASED) slow = __builtin_expect(__any(c[0][0] >= (FP8 ? 0x1p-9f : 1.0f)), 0);
+    float bias = __builtin_fmaf(MAG, c[0][0], mref);
+    if constexpr (BIASED && FP8) bias = __builtin_fmaf(__builtin_fabsf(bias), 0x1p-23f, bias);
+    auto prob = [&](int jt, int r, auto slow_tag) {
+      constexpr bool SLOW = decltype(slow_tag)::value;
+      float arg;
+      if constexpr (!KSU)
+        arg = y[jt][r] - mref;
+      else if constexpr (SLOW)
+        arg = __builtin_fmaf(__int_as_float(sc[jt][r]) - kMagic, c[0][0], -mref);
+      else
+        arg = __builtin_fmaf(__int_as_float(sc[jt][r]), c[0][0], -bias);
       if constexpr (MASKED) arg = valid[jt][r] ? arg : -INFINITY;
       return __builtin_amdgcn_exp2f(arg);
     };
@@ -617,22 +658,30 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // this one, the sums are fp32 adds over the unrounded P (four chains).
       // At D = 64 the matrix phase is short and this phase is the longer one:
       // the 16 dot2 over the fp16 P (two chains) cost less than 32 adds.
-      float ls[4] = {lsum, 0.0f, 0.0f, 0.0f};
-      const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+      auto emit = [&](auto slow_tag) {
+        float ls[4];
+        const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = prob(u >> 1, 8 * (u & 1) + e), p1 = prob(u >> 1, 8 * (u & 1) + e + 1);
-          const v2h hp = {(_Float16)p0, (_Float16)p1};
-          if constexpr (D == 128)
-            ls[e >> 1] += p0 + p1;
-          else
-            ls[(e >> 1) & 1] = __builtin_amdgcn_fdot2(hp, ones, ls[(e >> 1) & 1], false);
-          pf[u][e] = hp[0];
-          pf[u][e + 1] = hp[1];
-        }
-      lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = prob(u >> 1, 8 * (u & 1) + e, slow_tag), p1 = prob(u >> 1, 8 * (u & 1) + e + 1, slow_tag);
+            const v2h hp = {(_Float16)p0, (_Float16)p1};
+            if constexpr (D == 128) {
+              ls[e >> 1] = u == 0 ? p0 + p1 : ls[e >> 1] + (p0 + p1);
+            } else {
+              const int a = (e >> 1) & 1;
+              ls[a] = __builtin_amdgcn_fdot2(hp, ones, (u == 0 && e < 4) ? 0.0f : ls[a], false);
+            }
+            pf[u][e] = hp[0];
+            pf[u][e + 1] = hp[1];
+          }
+        lsum += D == 128 ? (ls[0] + ls[1]) + (ls[2] + ls[3]) : ls[0] + ls[1];
+      };
+      if (BIASED && slow)
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
       // P is complete here, in this (vector) phase: otherwise the compiler
       // sinks the exponentials into the next matrix phase, next to their use
 #pragma unroll
@@ -644,16 +693,25 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       asm volatile("" : "+v"(lsum));
     } else {
       float ps = 0.0f;
+      auto emit = [&](auto slow_tag) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-          const float p0 = prob(jt, r), p1 = prob(jt, r + 1), p2 = prob(jt, r + 2), p3 = prob(jt, r + 3);
-          ps += (p0 + p1) + (p2 + p3);
-          uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
-          pf8[4 * jt + r / 4] = (int)wv;
-        }
+          for (int r = 0; r < 16; r += 4) {
+            const float p0 = prob(jt, r, slow_tag), p1 = prob(jt, r + 1, slow_tag), p2 = prob(jt, r + 2, slow_tag),
+                        p3 = prob(jt, r + 3, slow_tag);
+            ps = (jt == 0 && r == 0) ? (p0 + p1) + (p2 + p3) : ps + ((p0 + p1) + (p2 + p3));
+            // (the conversion writes one half of the word and keeps the other:
+            // the previous tile's bits stand in for the half written next)
+            uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (uint32_t)pf8[4 * jt + r / 4], false);
+            wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
+            pf8[4 * jt + r / 4] = (int)wv;
+          }
+      };
+      if (BIASED && slow)
+        emit(std::true_type{});
+      else
+        emit(std::false_type{});
       lsum += __builtin_ldexpf(ps, pscale - 127);
       asm volatile("" : "+v"(pf8));
       asm volatile("" : "+v"(lsum));
@@ -684,14 +742,15 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   const int8_t* knext = kseq + (int64_t)hf * BN * kn;
   const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
   // (fp16 V rows hold dv channels: the last row is read up to them only)
-  int krec = (int)((L - 1 - hf * BN) * kn + S::KROW), vrec = (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
+  int krec = (int)((L - 1 - hf * BN) * kn + S::KROW);
+  int vrec = DUMP ? -(1 << 30) : (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
   // smooth Q: this half's next compensation tile, with K (fp32 per key of this query head)
-  const float* dnext = SQ ? a.q_delta + seq_head_base(p.cu, a.qds, s, h) + hf * BN : nullptr;
+  const float* dnext = SQ ? a.q_delta + seq_head_base(p.cu, a.qds, s, h, p.total) + hf * BN : nullptr;
   int drec = (L - hf * BN) * 4;
   constexpr int dstep = 2 * BN * 4;
   // 4-bit: this half's next tile of K's E8M0 words (one 32-bit word per key, head kvh)
-  const uint8_t* ksnext = QK4 ? a.ksc4 + seq_head_base(p.cu, a.kss4, s, kvh) + (int64_t)hf * BN * a.kss4.n : nullptr;
+  const uint8_t* ksnext = QK4 ? a.ksc4 + seq_head_base(p.cu, a.kss4, s, kvh, p.total) + (int64_t)hf * BN * a.kss4.n : nullptr;
   int ksrec = (L - hf * BN) * 4;
   const int ksstep = QK4 ? (int)(2 * BN * a.kss4.n) : 0;
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
@@ -992,6 +1051,21 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     const int t = b - 1;
     const Ck ck = load_ck(min(max(t, 0), ntiles - 1));  // (t outside the tiles: value unused)
     const uint32_t dslot = doffs(wrap6(pd + 5));         // tile t = b - 1 (smooth Q)
+    if constexpr (DUMP) {
+      if ((FULL || (t >= 0 && t < wtiles)) && i < L) {
+        int32_t* drow = a.dump + (sh * p.max_seqlen + i) * p.max_seqlen;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = t * BN + 32 * jt + 8 * q + 4 * g;
+            if (j < L)
+              *reinterpret_cast<v4i*>(drow + j) =
+                  v4i{sc[jt][4 * q] - kMagicBits, sc[jt][4 * q + 1] - kMagicBits, sc[jt][4 * q + 2] - kMagicBits,
+                      sc[jt][4 * q + 3] - kMagicBits};
+          }
+      }
+    }
     if (FULL) {
       softmax(t, ck, dslot, std::false_type{});
     } else if (t >= 0 && t < wtiles) {
@@ -1098,7 +1172,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       *(LDS v4h*)(ostage + (i - q0) * S::OROW + 2 * cc) = hv;
     }
   __syncthreads();  // (half 1 has ended: the barrier waits for half 0's waves)
-  _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h);
+  _Float16* __restrict__ obase = (_Float16*)a.out + seq_head_base(p.cu, a.os, s, h, p.total);
   constexpr int CPR = D / 8;  // 16-byte pieces per row
   constexpr int NPC = BM * CPR / (NT / 2);
   v4i opc[NPC];  // (all LDS reads first, then the stores)
@@ -1110,80 +1184,26 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
 #pragma unroll
   for (int x = 0; x < NPC; ++x) {
     const int c = tid + x * (NT / 2), rr = c / CPR, cp = c % CPR;
-    if (q0 + rr < L && 8 * cp < p.dv) *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) = opc[x];
+    if (!DUMP && q0 + rr < L && 8 * cp < p.dv)
+      *reinterpret_cast<v4i*>(obase + (int64_t)(q0 + rr) * a.os.n + 8 * cp) = opc[x];
   }
 }
 
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4, bool DUMP = false>
 __global__ __launch_bounds__(NT) void k_attn(Problem p, AttnArgs a) {
   using S = Lds<D, FP8, QK4>;
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::BYTES + (SQ ? S::DBYTES : 0) + (QK4 ? S::DBYTES : 0)];
-  attn_body<D, FP8, CAUSAL, KSU, SQ, QK4>(p, a, (lds_u8*)lds_raw);
+  attn_body<D, FP8, CAUSAL, KSU, SQ, QK4, DUMP>(p, a, (lds_u8*)lds_raw);
 }
 
-// Debug: the INT32 scores of the same staging (DmaPlan) and MFMA path
-// (qk_tile), before any dequantisation.  Dense problems, every query row and
-// key written; 8 waves x 32 rows per workgroup.
-template <int D>
-__global__ __launch_bounds__(NT) void k_qk_dump(Problem p, AttnArgs a) {
-  using S = Lds<D, true>;  // K part only
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[S::KBYTES];
-  lds_u8* const lds = (lds_u8*)lds_raw;
-  const int qt = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(p.cu, s, p.max_seqlen);
-  const int q0 = qt * NW * 32;
-  if (q0 >= L) return;
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t sh = (int64_t)s * H + h;
-  const int8_t* qbase = a.q8 + seq_head_base(p.cu, a.q8s, s, h);
-  const int8_t* kseq = a.k8 + seq_head_base(p.cu, a.k8s, s, h / (p.heads / p.kv_heads));
-  const int i = q0 + w * 32 + li;
-  v4i qf[D / 32];
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk)
-    qf[kk] = i < L ? *reinterpret_cast<const v4i*>(qbase + (int64_t)i * a.q8s.n + 32 * kk + 16 * g) : v4i{0, 0, 0, 0};
-  v16i magic;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
-  uint32_t kofs[D / 32];
-#pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * D + 16 * ((2 * kk + g) ^ S::kswz(li));
-  for (int x = tid; x < S::KBYTES / 16; x += NT) *(LDS v4i*)(lds + 16 * x) = v4i{0, 0, 0, 0};
-  DmaPlan<D, true> dma;
-  dma.init(w & 3, lane, a.k8s.n, 0);
-  for (int j0 = 0; j0 < L; j0 += BN) {
-    __syncthreads();  // everyone is done reading the previous tile
-    if (w < NWH)  // the plan covers a tile with 4 waves
-      dma.issue_k(make_rsrc(kseq + (int64_t)j0 * a.k8s.n, (int)((L - 1 - j0) * a.k8s.n + D)), lds, w);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    v16i sc[2];
-    qk_tile<D>(lds, kofs, qf, magic, sc);
-    if (i < L) {
-      int32_t* drow = a.dump + (sh * p.max_seqlen + i) * p.max_seqlen;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + 32 * jt + 8 * q + 4 * g;
-          if (j < L)
-            *reinterpret_cast<v4i*>(drow + j) =
-                v4i{sc[jt][4 * q] - kMagicBits, sc[jt][4 * q + 1] - kMagicBits, sc[jt][4 * q + 2] - kMagicBits,
-                    sc[jt][4 * q + 3] - kMagicBits};
-        }
-    }
-  }
-}
-
-template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4 = false>
+template <int D, bool FP8, bool CAUSAL, bool KSU, bool SQ, bool QK4 = false, bool DUMP = false>
 hipError_t launch_cfg(const Problem& p, const AttnArgs& a, hipStream_t st) {
   const int nqt = (p.max_seqlen + BM - 1) / BM;
   // slots per XCD: ceil(groups / 8) groups of heads/kv_heads query heads
   const int64_t P8 = ((int64_t)p.nseq * p.kv_heads + 7) / 8 * 8 * (p.heads / p.kv_heads);
   const int64_t G = (int64_t)nqt * P8;
   if (G >= (1ll << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU, SQ, QK4>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
+  hipLaunchKernelGGL((k_attn<D, FP8, CAUSAL, KSU, SQ, QK4, DUMP>), dim3((unsigned)G), dim3(NT), 0, st, p, a);
   return hipGetLastError();
 }
 
@@ -1207,11 +1227,7 @@ hipError_t launch_ks(const Problem& p, const AttnArgs& a, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(const Problem& p, const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
-  if (a.dump) {
-    const int nqt = (p.max_seqlen + NW * 32 - 1) / (NW * 32);
-    hipLaunchKernelGGL((k_qk_dump<D>), dim3(nqt, p.heads, p.nseq), dim3(NT), 0, st, p, a);
-    return hipGetLastError();
-  }
+  if (a.dump) return launch_cfg<D, false, false, true, false, false, true>(p, a, st);
   if (fp8) return causal ? launch_ks<D, true, true>(p, a, st) : launch_ks<D, true, false>(p, a, st);
   return causal ? launch_ks<D, false, true>(p, a, st) : launch_ks<D, false, false>(p, a, st);
 }

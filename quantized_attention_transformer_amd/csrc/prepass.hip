@@ -276,12 +276,12 @@ __device__ __forceinline__ void colsum_chunk(const _Float16* __restrict__ base, 
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
-    int max_seqlen, int blk_q, int nbq, int nqw, int nks, int kv_heads, int dv, float sm_scale,
+    int max_seqlen, int total, int blk_q, int nbq, int nqw, int nks, int kv_heads, int dv, float sm_scale,
     int8_t* __restrict__ q8, Str q8s,
     float* __restrict__ sq, double* __restrict__ part) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const bool cgv = 8 * cg < dv;  // this thread's 8 channels are real (not head_dim 96 padding)
   const int64_t sh = (int64_t)s * H + h;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     H8 row;
     float a = 0.0f;
     if (valid) {
-      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8, cgv);
+      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h, total) + (int64_t)n * qs.n + cg * 8, cgv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf((float)row.v[i]));
       a *= sm_scale;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     for (int m = TPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));  // the row's TPR lanes
     if (valid) {
       const float scale = a > 0.0f ? a / 127.0f : 0.0f;
-      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h) + (int64_t)n * q8s.n + cg * 8) =
+      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h, total) + (int64_t)n * q8s.n + cg * 8) =
           a > 0.0f ? codes8(row, scale_q, scale, __builtin_amdgcn_rcpf(scale)) : make_uint2(0u, 0u);
       if (cg == 0) sq[sh * nbq + n] = scale;
     }
@@ -313,8 +313,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const int n0 = x * blk_q;
     if (n0 >= L) return;
     const int n1 = min(L, n0 + blk_q);
-    const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, scale_q,
-                                       q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n, cgv);
+    const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h, total) + cg * 8, qs.n, n0, n1, scale_q,
+                                       q8 + seq_head_base(cu, q8s, s, h, total) + cg * 8, q8s.n, cgv);
     if (tid == 0) sq[sh * nbq + x] = scale;
     return;
   }
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
   const int ci = x - nqw;
   const int n0 = ci * kKChunkRows;
   if (n0 >= L) return;
-  colsum_chunk<D, kKChunkRows / 128>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, min(L, n0 + kKChunkRows),
+  colsum_chunk<D, kKChunkRows / 128>(K + seq_head_base(cu, ks, s, h, total) + cg * 8, ks.n, n0, min(L, n0 + kKChunkRows),
                                      cgv, part + (skv * nks + ci) * D);
 }
 
@@ -333,22 +333,22 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_colsums_qk(const _Float16* __restrict__ Q, Str qs,
                                                           const _Float16* __restrict__ K, Str ks,
-                                                          const int32_t* __restrict__ cu, int max_seqlen, int nks,
+                                                          const int32_t* __restrict__ cu, int max_seqlen, int total, int nks,
                                                           int kv_heads, int dv, double* __restrict__ qpart,
                                                           double* __restrict__ kpart) {
   const int ci = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = ci * kKSumRows;
   if (n0 >= L) return;
   const int n1 = min(L, n0 + kKSumRows);
   const int cg = threadIdx.x % (D / 8);
   const bool cgv = 8 * cg < dv;
   if (qpart)
-    colsum_chunk<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, n1, cgv,
+    colsum_chunk<D>(Q + seq_head_base(cu, qs, s, h, total) + cg * 8, qs.n, n0, n1, cgv,
                     qpart + (((int64_t)s * H + h) * nks + ci) * D);
   if (h < kv_heads) {
     __syncthreads();  // (colsum_chunk's LDS is reused)
-    colsum_chunk<D>(K + seq_head_base(cu, ks, s, h) + cg * 8, ks.n, n0, n1, cgv,
+    colsum_chunk<D>(K + seq_head_base(cu, ks, s, h, total) + cg * 8, ks.n, n0, n1, cgv,
                     kpart + (((int64_t)s * kv_heads + h) * nks + ci) * D);
   }
 }
@@ -383,11 +383,11 @@ __device__ __forceinline__ double sum_partials(const double* __restrict__ pp, in
 // sequences (shorter ones fold this into the quantisation kernel).
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __restrict__ part,
-                                                             const int32_t* __restrict__ cu, int max_seqlen,
+                                                             const int32_t* __restrict__ cu, int max_seqlen, int total,
                                                              int nks, int chunk, double scale,
                                                              float* __restrict__ km) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x % D, g = threadIdx.x / D;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int nb = (L + chunk - 1) / chunk;
   const double sum = sum_partials<D>(part + ((int64_t)s * H + h) * nks * D + c, nb, c, g);
   if (g == 0) km[((int64_t)s * H + h) * D + c] = L > 0 ? (float)((sum / (double)L) * scale) : 0.0f;
@@ -400,14 +400,14 @@ __global__ __launch_bounds__(kQThreads) void k_mean_finalize(const double* __res
 // from k_mean_finalize.
 template <int D, bool FOLD>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_smooth(const _Float16* __restrict__ Q, Str qs,
-                                                              const int32_t* __restrict__ cu, int max_seqlen,
+                                                              const int32_t* __restrict__ cu, int max_seqlen, int total,
                                                               int blk_q, int nbq, int nks, int dv, float sm_scale,
                                                               const double* __restrict__ qpart,
                                                               float* __restrict__ qmean, int8_t* __restrict__ q8,
                                                               Str q8s, float* __restrict__ sq) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const bool cgv = 8 * cg < dv;
   const int64_t sh = (int64_t)s * H + h;
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_smooth(const _Float16* __
     H8 row;
     float a = 0.0f;
     if (valid) {
-      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h) + (int64_t)n * qs.n + cg * 8, cgv);
+      row = load_h8_or_zero(Q + seq_head_base(cu, qs, s, h, total) + (int64_t)n * qs.n + cg * 8, cgv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(smooth((float)row.v[i], i)));
     }
@@ -450,14 +450,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_smooth(const _Float16* __
     for (int m = TPR / 2; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));  // the row's TPR lanes
     if (valid) {
       const float scale = a > 0.0f ? a / 127.0f : 0.0f;
-      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h) + (int64_t)n * q8s.n + cg * 8) =
+      *reinterpret_cast<uint2*>(q8 + seq_head_base(cu, q8s, s, h, total) + (int64_t)n * q8s.n + cg * 8) =
           a > 0.0f ? codes8(row, smooth, scale, __builtin_amdgcn_rcpf(scale)) : make_uint2(0u, 0u);
       if (cg == 0) sq[sh * nbq + n] = scale;
     }
     return;
   }
-  const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h) + cg * 8, qs.n, n0, min(L, n0 + blk_q), smooth,
-                                     q8 + seq_head_base(cu, q8s, s, h) + cg * 8, q8s.n, cgv);
+  const float scale = quant_block<D>(Q + seq_head_base(cu, qs, s, h, total) + cg * 8, qs.n, n0, min(L, n0 + blk_q), smooth,
+                                     q8 + seq_head_base(cu, q8s, s, h, total) + cg * 8, q8s.n, cgv);
   if (tid == 0) sq[sh * nbq + x] = scale;
 }
 
@@ -468,14 +468,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_smooth(const _Float16* __
 // TPR lanes), rounded once to fp32.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_q_delta(const _Float16* __restrict__ K, Str ks,
-                                                       const int32_t* __restrict__ cu, int max_seqlen, int kv_heads,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int total, int kv_heads,
                                                        int dv, const float* __restrict__ qmean,
                                                        const float* __restrict__ kmean, float* __restrict__ qdelta,
                                                        Str qds) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR, R = 128 / RPP;
   const int h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
   const int kvh = h / (H / kv_heads);
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = blockIdx.x * 128;
   if (n0 >= L) return;
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
@@ -487,8 +487,8 @@ __global__ __launch_bounds__(kQThreads) void k_q_delta(const _Float16* __restric
     km[i] = kmean[((int64_t)s * kv_heads + kvh) * D + cg * 8 + i];
   }
   BlockRows<D> rows;
-  rows.load(K + seq_head_base(cu, ks, s, kvh) + cg * 8, ks.n, n0, min(L, n0 + 128), cgv);
-  float* const out = qdelta + seq_head_base(cu, qds, s, h);
+  rows.load(K + seq_head_base(cu, ks, s, kvh, total) + cg * 8, ks.n, n0, min(L, n0 + 128), cgv);
+  float* const out = qdelta + seq_head_base(cu, qds, s, h, total);
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const int n = n0 + r + RPP * j;
@@ -508,20 +508,20 @@ __global__ __launch_bounds__(kQThreads) void k_q_delta(const _Float16* __restric
 // flight; otherwise k_mean comes from k_mean_finalize.
 template <int D, bool FOLD>
 __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restrict__ K, Str ks,
-                                                       const int32_t* __restrict__ cu, int max_seqlen, int blk_k,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int total, int blk_k,
                                                        int nbk, int nks, int chunk, int dv,
                                                        const double* __restrict__ part,
                                                        float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
                                                        float* __restrict__ sk) {
   constexpr int TPR = D / 8;
   const int bi = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = bi * blk_k;
   if (n0 >= L) return;
   const int n1 = min(L, n0 + blk_k);
   const int cg = threadIdx.x % TPR;
   const int64_t sh = (int64_t)s * H + h;
-  const _Float16* kb = K + seq_head_base(cu, ks, s, h) + cg * 8;
+  const _Float16* kb = K + seq_head_base(cu, ks, s, h, total) + cg * 8;
   const bool cgv = 8 * cg < dv;
   BlockRows<D> krows;
   const bool pre = n1 - n0 <= 128;
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
     for (int i = 0; i < 8; ++i) mean[i] = km[sh * D + cg * 8 + i];
   }
   const float scale = quant_block<D>(kb, ks.n, n0, n1, [&](float v, int i) { return v - mean[i]; },
-                                     k8 + seq_head_base(cu, k8s, s, h) + cg * 8, k8s.n, cgv, pre ? &krows : nullptr);
+                                     k8 + seq_head_base(cu, k8s, s, h, total) + cg * 8, k8s.n, cgv, pre ? &krows : nullptr);
   if (threadIdx.x == 0) sk[sh * nbk + bi] = scale;
 }
 
@@ -573,13 +573,13 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
 // block's E8M0 code at byte cg/4 of the row in xsc (row stride xss.n bytes).
 template <int D, bool IS_Q>
 __global__ __launch_bounds__(kQThreads) void k_quant_mxfp4(const _Float16* __restrict__ X, Str xs,
-                                                           const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                           const int32_t* __restrict__ cu, int max_seqlen, int total, int dv,
                                                            float sm_scale, const float* __restrict__ mean,
                                                            uint8_t* __restrict__ x4, Str x4s, uint8_t* __restrict__ xsc,
                                                            Str xss) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
   const int h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int tid = threadIdx.x, cg = tid % TPR, n = blockIdx.x * RPP + tid / TPR;
   if (blockIdx.x * RPP >= L) return;
   const bool valid = n < L;
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mxfp4(const _Float16* __res
   float xv[8] = {};
   float a = 0.0f;
   if (valid) {
-    const H8 row = load_h8_or_zero(X + seq_head_base(cu, xs, s, h) + (int64_t)n * xs.n + cg * 8, 8 * cg < dv);
+    const H8 row = load_h8_or_zero(X + seq_head_base(cu, xs, s, h, total) + (int64_t)n * xs.n + cg * 8, 8 * cg < dv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma clang fp contract(off)
@@ -612,8 +612,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mxfp4(const _Float16* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) w |= e2m1_code(ldexpf(xv[i], 127 - code)) << (4 * i);
   }
-  *reinterpret_cast<uint32_t*>(x4 + seq_head_base(cu, x4s, s, h) + (int64_t)n * x4s.n + 4 * cg) = w;
-  if ((cg & 3) == 0) xsc[seq_head_base(cu, xss, s, h) + (int64_t)n * xss.n + cg / 4] = (uint8_t)code;
+  *reinterpret_cast<uint32_t*>(x4 + seq_head_base(cu, x4s, s, h, total) + (int64_t)n * x4s.n + 4 * cg) = w;
+  if ((cg & 3) == 0) xsc[seq_head_base(cu, xss, s, h, total) + (int64_t)n * xss.n + cg / 4] = (uint8_t)code;
 }
 
 // ---------------------------------------------------------------- E4M3 V
@@ -629,16 +629,16 @@ __global__ void k_fill_zero(float* __restrict__ x, int64_t n) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_colmax(const _Float16* __restrict__ V, Str vs,
-                                                        const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                        const int32_t* __restrict__ cu, int max_seqlen, int total, int dv,
                                                         float* __restrict__ vmax) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
   const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = chunk * kColChunk;
   if (n0 >= L) return;
   const int n1 = min(L, n0 + kColChunk);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
-  const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
+  const _Float16* base = V + seq_head_base(cu, vs, s, h, total) + cg * 8;
   float m[8] = {};
   if (8 * cg < dv) {  // padding channels (head_dim 96) keep 0; the test stays outside the loop so that
                       // the unrolled loads issue together
@@ -669,19 +669,19 @@ __global__ void k_v_scale(float* __restrict__ sv, int64_t n) {
 // fp32(V - vmean), the smoothed V) with the per-channel scales sv.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict__ V, Str vs,
-                                                       const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                       const int32_t* __restrict__ cu, int max_seqlen, int total, int dv,
                                                        const float* __restrict__ sv,
                                                        const float* __restrict__ vmean, uint8_t* __restrict__ v8,
                                                        Str v8s) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
   const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = chunk * kColChunk;
   if (n0 >= L) return;
   const int n1 = min(L, n0 + kColChunk);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
-  const _Float16* src = V + seq_head_base(cu, vs, s, h) + cg * 8;
-  uint8_t* dst = v8 + seq_head_base(cu, v8s, s, h) + cg * 8;
+  const _Float16* src = V + seq_head_base(cu, vs, s, h, total) + cg * 8;
+  uint8_t* dst = v8 + seq_head_base(cu, v8s, s, h, total) + cg * 8;
   float scale[8], mean[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -721,18 +721,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_v(const _Float16* __restrict
 // channel, the exact fp64 sum and the fp16 maximum and minimum (as float).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restrict__ V, Str vs,
-                                                          const int32_t* __restrict__ cu, int max_seqlen, int dv,
+                                                          const int32_t* __restrict__ cu, int max_seqlen, int total, int dv,
                                                           int nchunk,
                                                           double* __restrict__ psum, float* __restrict__ pmax,
                                                           float* __restrict__ pmin) {
   constexpr int TPR = D / 8, RPP = kThreads / TPR;
   const int chunk = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = chunk * kColChunk;
   if (n0 >= L) return;
   const int n1 = min(L, n0 + kColChunk);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
-  const _Float16* base = V + seq_head_base(cu, vs, s, h) + cg * 8;
+  const _Float16* base = V + seq_head_base(cu, vs, s, h, total) + cg * 8;
   double acc[8] = {};
   Extremes ex;
   if (8 * cg < dv) {  // the channel test stays outside the loop so that the unrolled loads issue together
@@ -779,10 +779,10 @@ __global__ __launch_bounds__(kThreads) void k_v_colstats(const _Float16* __restr
 template <int D>
 __global__ __launch_bounds__(D) void k_v_finalize(const double* __restrict__ psum, const float* __restrict__ pmax,
                                                   const float* __restrict__ pmin, const int32_t* __restrict__ cu,
-                                                  int max_seqlen, int nchunk, float* __restrict__ sv,
+                                                  int max_seqlen, int total, int nchunk, float* __restrict__ sv,
                                                   float* __restrict__ vmean) {
   const int h = blockIdx.x, s = blockIdx.y, H = gridDim.x, c = threadIdx.x;
-  const int L = seq_len(cu, s, max_seqlen);
+  const int L = seq_len(cu, s, max_seqlen, total);
   const int64_t sh = (int64_t)s * H + h;
   if (L <= 0) {
     sv[sh * D + c] = 0.0f;
@@ -832,7 +832,7 @@ hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const 
     const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
     const int nkc = (p.max_seqlen + kKChunkRows - 1) / kKChunkRows;  // K column-sum chunks per head
     hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + nkc, p.heads, p.nseq), dim3(kQThreads), 0, st,
-                       (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_q, p.nbq, nqw,
+                       (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.blk_q, p.nbq, nqw,
                        p.nks, p.kv_heads, p.dv, sm_scale, q8, q8s, q_scale, partial);
   });
   return hipGetLastError();
@@ -843,16 +843,16 @@ hipError_t launch_quant_k(const Problem& p, const void* K, Str ks, const double*
   dim3 grid(p.nbk, p.kv_heads, p.nseq);
   if (p.max_seqlen <= kFoldMaxTokens) {
     SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, true>), grid, dim3(kQThreads), 0, st,
-                                                   (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
+                                                   (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.blk_k, p.nbk, p.nks,
                                                    chunk, p.dv, partial, k_mean, k8, k8s, k_scale));
     return hipGetLastError();
   }
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
-                                                 partial, p.cu, p.max_seqlen, p.nks, chunk, 1.0, k_mean));
+                                                 partial, p.cu, p.max_seqlen, p.total, p.nks, chunk, 1.0, k_mean));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_k<D, false>), grid, dim3(kQThreads), 0, st,
-                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.blk_k, p.nbk, p.nks,
+                                                 (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.blk_k, p.nbk, p.nks,
                                                  chunk, p.dv, partial, k_mean, k8, k8s, k_scale));
   return hipGetLastError();
 }
@@ -863,7 +863,7 @@ hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const 
   hipError_t e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_colsums_qk<D>), dim3(p.nks, p.heads, p.nseq), dim3(kQThreads), 0,
                                                  st, (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu,
-                                                 p.max_seqlen, p.nks, p.kv_heads, p.dv, qpart, kpart));
+                                                 p.max_seqlen, p.total, p.nks, p.kv_heads, p.dv, qpart, kpart));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, {
     constexpr int RPP = kQThreads / (D / 8);
@@ -871,13 +871,13 @@ hipError_t launch_quant_q_smooth(const Problem& p, const void* Q, Str qs, const 
     const dim3 grid(nqw, p.heads, p.nseq);
     if (p.nks <= kFoldMaxBlocks) {
       hipLaunchKernelGGL((k_quant_q_smooth<D, true>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
-                         p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
+                         p.max_seqlen, p.total, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
     } else {
       hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
-                         p.max_seqlen, p.nks, kKSumRows, (double)sm_scale, q_mean);
+                         p.max_seqlen, p.total, p.nks, kKSumRows, (double)sm_scale, q_mean);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       hipLaunchKernelGGL((k_quant_q_smooth<D, false>), grid, dim3(kQThreads), 0, st, (const _Float16*)Q, qs, p.cu,
-                         p.max_seqlen, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
+                         p.max_seqlen, p.total, p.blk_q, p.nbq, p.nks, p.dv, sm_scale, qpart, q_mean, q8, q8s, q_scale);
     }
   });
   return hipGetLastError();
@@ -891,23 +891,23 @@ hipError_t launch_quant_mxfp4(const Problem& p, const void* Q, Str qs, const voi
     constexpr int RPP = kQThreads / (D / 8);
     const int nx = (p.max_seqlen + RPP - 1) / RPP;
     hipLaunchKernelGGL((k_colsums_qk<D>), dim3(p.nks, p.heads, p.nseq), dim3(kQThreads), 0, st, (const _Float16*)Q, qs,
-                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.nks, p.kv_heads, p.dv,
+                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.nks, p.kv_heads, p.dv,
                        p.smooth_q ? qpart : nullptr, kpart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(kQThreads), 0, st, kpart, p.cu,
-                       p.max_seqlen, p.nks, kKSumRows, 1.0, k_mean);
+                       p.max_seqlen, p.total, p.nks, kKSumRows, 1.0, k_mean);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.smooth_q) {
       hipLaunchKernelGGL((k_mean_finalize<D>), dim3(p.heads, p.nseq), dim3(kQThreads), 0, st, qpart, p.cu,
-                         p.max_seqlen, p.nks, kKSumRows, (double)sm_scale, q_mean);
+                         p.max_seqlen, p.total, p.nks, kKSumRows, (double)sm_scale, q_mean);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL((k_quant_mxfp4<D, true>), dim3(nx, p.heads, p.nseq), dim3(kQThreads), 0, st,
-                       (const _Float16*)Q, qs, p.cu, p.max_seqlen, p.dv, sm_scale, p.smooth_q ? q_mean : nullptr, q4,
+                       (const _Float16*)Q, qs, p.cu, p.max_seqlen, p.total, p.dv, sm_scale, p.smooth_q ? q_mean : nullptr, q4,
                        q4s, qsc, qss);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((k_quant_mxfp4<D, false>), dim3(nx, p.kv_heads, p.nseq), dim3(kQThreads), 0, st,
-                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.dv, 1.0f, k_mean, k4, k4s, ksc, kss);
+                       (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.dv, 1.0f, k_mean, k4, k4s, ksc, kss);
   });
   return hipGetLastError();
 }
@@ -915,7 +915,7 @@ hipError_t launch_quant_mxfp4(const Problem& p, const void* Q, Str qs, const voi
 hipError_t launch_q_delta(const Problem& p, const void* K, Str ks, const float* q_mean, const float* k_mean,
                           float* q_delta, Str qds, hipStream_t st) {
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_q_delta<D>), dim3((p.max_seqlen + 127) / 128, p.heads, p.nseq),
-                                                 dim3(kQThreads), 0, st, (const _Float16*)K, ks, p.cu, p.max_seqlen,
+                                                 dim3(kQThreads), 0, st, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total,
                                                  p.kv_heads, p.dv, q_mean, k_mean, q_delta, qds));
   return hipGetLastError();
 }
@@ -925,7 +925,7 @@ hipError_t launch_v_colmax(const Problem& p, const void* V, Str vs, float* vmax,
   hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vmax, n);
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colmax<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, vmax));
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.total, p.dv, vmax));
   return hipGetLastError();
 }
 
@@ -939,7 +939,7 @@ hipError_t launch_quant_v(const Problem& p, const void* V, Str vs, const float* 
                           uint8_t* v8, Str v8s, hipStream_t st) {
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_quant_v<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, v_scale, v_mean,
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.total, p.dv, v_scale, v_mean,
                                                  v8, v8s));
   return hipGetLastError();
 }
@@ -948,12 +948,12 @@ hipError_t launch_v_smooth_stats(const Problem& p, const void* V, Str vs, double
                                  float* v_scale, float* v_mean, hipStream_t st) {
   dim3 grid(p.nchunk, p.kv_heads, p.nseq);
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_colstats<D>), grid, dim3(kThreads), 0, st,
-                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.dv, p.nchunk, psum,
+                                                 (const _Float16*)V, vs, p.cu, p.max_seqlen, p.total, p.dv, p.nchunk, psum,
                                                  pmax, pmin));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SAGE_DISPATCH_D(p.head_dim, hipLaunchKernelGGL((k_v_finalize<D>), dim3(p.kv_heads, p.nseq), dim3(D), 0, st, psum,
-                                                 pmax, pmin, p.cu, p.max_seqlen, p.nchunk, v_scale, v_mean));
+                                                 pmax, pmin, p.cu, p.max_seqlen, p.total, p.nchunk, v_scale, v_mean));
   return hipGetLastError();
 }
 

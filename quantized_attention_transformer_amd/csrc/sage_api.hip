@@ -4,6 +4,7 @@
 // carves the caller's workspace, sizes the grids and enqueues the kernels on
 // the caller's stream.  Nothing here allocates device memory, synchronises or
 // reads device memory.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -52,7 +53,9 @@ int check_problem(const sage_problem* p, bool allow_d96 = false) {
     return fail(SAGE_ERR_INVALID_ARG,
                 "blk_q/blk_k (%d, %d) must be multiples of 16 in [16, 256] (blk_q may also be 1: per token)",
                 p->blk_q, p->blk_k);
-  if (p->cu_seqlens && p->total_tokens < 0) return fail(SAGE_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (p->cu_seqlens && (p->total_tokens < 0 || p->total_tokens > INT32_MAX))
+    return fail(SAGE_ERR_INVALID_ARG, "total_tokens (%lld) must be in [0, 2^31) (cu_seqlens is int32)",
+                (long long)p->total_tokens);
   if (p->heads > 65535 || p->nseq > 65535) return fail(SAGE_ERR_UNSUPPORTED, "heads and nseq must be <= 65535");
   if (p->kv_heads < 0 || (p->kv_heads > 0 && p->heads % p->kv_heads != 0))
     return fail(SAGE_ERR_INVALID_ARG, "kv_heads (%d) must divide heads (%d) (0: same as heads)", p->kv_heads,
@@ -87,6 +90,7 @@ sage::Problem to_internal(const sage_problem* p) {
   q.heads = p->heads;
   q.kv_heads = p->kv_heads > 0 ? p->kv_heads : p->heads;
   q.max_seqlen = p->max_seqlen;
+  q.total = p->cu_seqlens ? (int)p->total_tokens : 0;
   q.head_dim = p->head_dim == 96 ? 128 : p->head_dim;
   q.dv = p->head_dim;
   q.blk_q = p->blk_q;

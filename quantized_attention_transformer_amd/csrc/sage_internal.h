@@ -22,18 +22,29 @@ constexpr int kKSumRows = 128;
 // fewer partials for the K quantisation to add up.
 constexpr int kKChunkRows = 512;
 
-__device__ __forceinline__ int seq_len(const int32_t* cu, int s, int max_seqlen) {
-  return cu ? (cu[s + 1] - cu[s]) : max_seqlen;
+// Packed sequences: sequence s holds tokens [cu[s], cu[s+1]) of `total`.  The
+// offsets are clamped so that every token range stays inside [0, total) and
+// no length exceeds max_seqlen, whatever cu_seqlens holds: a malformed array
+// gives wrong sequences, never an access outside the caller's buffers or the
+// per-sequence scale, workspace and output rows sized from max_seqlen.
+__host__ __device__ __forceinline__ int seq_start(const int32_t* cu, int s, int total) {
+  return min(max(cu[s], 0), total);
+}
+__host__ __device__ __forceinline__ int seq_len(const int32_t* cu, int s, int max_seqlen, int total) {
+  if (!cu) return max_seqlen;
+  const int a = seq_start(cu, s, total);
+  return min(min(max(cu[s + 1], a), total) - a, max_seqlen);
 }
 
 // Offset of token 0 of (sequence s, head h).
-__device__ __forceinline__ int64_t seq_head_base(const int32_t* cu, Str st, int s, int h) {
-  return (cu ? (int64_t)cu[s] * st.n : (int64_t)s * st.s) + (int64_t)h * st.h;
+__device__ __forceinline__ int64_t seq_head_base(const int32_t* cu, Str st, int s, int h, int total) {
+  return (cu ? (int64_t)seq_start(cu, s, total) * st.n : (int64_t)s * st.s) + (int64_t)h * st.h;
 }
 
 struct Problem {
   const int32_t* cu;
   int nseq, heads, max_seqlen, head_dim, blk_q, blk_k;
+  int total;             // packed sequences: total_tokens (< 2^31); dense: unused
   int kv_heads;          // heads of K and V (grouped-query attention: heads % kv_heads == 0)
   int dv;                // channels of the fp16 inputs and of O: head_dim, or 96 with head_dim 128
                          // (head dimension 96 runs on the 128-channel kernels, channels 96..127 zero)

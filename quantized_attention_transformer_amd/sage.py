@@ -305,8 +305,9 @@ def attn(q, k, v, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAG
 
 
 def debug_qk_i32(q8, k8, *, layout="bnhd"):
-    """sage_debug_qk_i32: INT32 scores [B, H, N, N] from the fused kernel's integer stage."""
-    prob = make_problem(q8, layout)
+    """sage_debug_qk_i32: INT32 scores [B, H, N, N] from the fused kernel's integer stage
+    (k8 may have fewer heads than q8)."""
+    prob = make_problem(q8, layout, k=k8)
     s = torch.empty((prob.nseq, prob.heads, prob.max_seqlen, prob.max_seqlen), dtype=torch.int32,
                     device=q8.device)
     rc = lib().sage_debug_qk_i32(ctypes.byref(prob), _ptr(q8), strides_of(q8, layout), _ptr(k8),

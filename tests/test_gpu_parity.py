@@ -158,7 +158,11 @@ def test_quantize_nondefault_blocks_and_layout():
 
 # ---------------------------------------------------------------- integer scores, bit-exact
 
-@pytest.mark.parametrize("N,H,d", [(256, 2, 64), (1000, 2, 128), (1024, 1, 128), (132, 3, 64)])
+# The dump comes from the fused kernel itself (a dump instantiation): N = 1000
+# and 1024 give 16 key tiles, so both halves run steady-state (qk_pv) phase
+# pairs as well as edge phases (qk_tile), through the 5-slot K ring.
+@pytest.mark.parametrize("N,H,d", [(256, 2, 64), (1000, 2, 128), (1024, 1, 128), (132, 3, 64), (1000, 2, 64),
+                                   (1024, 2, 64), (768, 2, 128)])
 def test_debug_qk_i32_bitexact(N, H, d):
     wl = synth.TEXT if d == 128 else synth.TINY
     inp = synth.generate(wl, seqlen=N, batch=1, heads=H)
@@ -167,6 +171,24 @@ def test_debug_qk_i32_bitexact(N, H, d):
     for h in range(H):
         want = O.scores_int(ref["q8"][0, :, h], ref["k8"][0, :, h])
         assert np.array_equal(s[0, h], want), f"head {h}: {(s[0, h] != want).sum()} mismatches"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_debug_qk_i32_extreme_codes_and_gqa(d):
+    """Codes of magnitude 127 everywhere (|S| up to 127^2 d, the edge of the
+    accumulator seed's range), two batches, and K with half the heads."""
+    rng = np.random.default_rng(d)
+    B, N, H, Hk = 2, 1024, 4, 2
+    q8 = (rng.choice([-127, 127], size=(B, N, H, d)) * (rng.random((B, N, H, d)) < 0.97)).astype(np.int8)
+    k8 = rng.choice([-127, 127], size=(B, N, Hk, d)).astype(np.int8)
+    k8[:, :64] = 127                           # keys of the first tile agree with some rows exactly
+    q8[:, :8] = 127
+    s = host(S().debug_qk_i32(dev(q8), dev(k8)))
+    for b in range(B):
+        for h in range(H):
+            want = O.scores_int(q8[b, :, h], k8[b, :, h // (H // Hk)])
+            assert np.array_equal(s[b, h], want), f"batch {b} head {h}: {(s[b, h] != want).sum()} mismatches"
+    assert np.abs(s).max() == 127 * 127 * d
 
 
 # ---------------------------------------------------------------- attention

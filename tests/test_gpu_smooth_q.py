@@ -175,7 +175,11 @@ def test_attn_smooth_q_closer_to_exact_attention():
 
 
 def test_attn_smooth_q_zero_mean_q_equals_plain():
-    # tokens in +- pairs: mean(Q') = 0 exactly, so the smooth-Q path computes the plain one
+    # tokens in +- pairs: mean(Q') = 0 exactly, so the smooth-Q path computes the plain one.
+    # fp16 P.V: bit-identical (both paths form the exponent S c - m exactly before its one
+    # rounding).  FP8 P.V: the plain path's exponent carries the non-integer log2(448) in a
+    # bias rounded once at the size of 1.5*2^23 c, the smooth-Q path's has none of it: the
+    # same method within the FP8 tolerance, not the same bits.
     inp = synth.generate(synth.TEXT, seqlen=600, batch=2, heads=2)
     q = np.concatenate([inp.q[:, :300], -inp.q[:, :300]], axis=1)
     qd, k, v = dev(q), dev(inp.k), dev(inp.v)
@@ -185,7 +189,13 @@ def test_attn_smooth_q_zero_mean_q_equals_plain():
         for mode in (0, 1):
             a = S().attn(qd, k, v, causal=causal, pv_mode=mode)
             b = S().attn(qd, k, v, causal=causal, pv_mode=mode, smooth_q=True)
-            assert torch.equal(a, b), (causal, mode)
+            if mode == 0:
+                assert torch.equal(a, b), (causal, mode)
+            else:
+                x, y = host(a).astype(np.float64), host(b).astype(np.float64)
+                c = float((x * y).sum() / np.linalg.norm(x) / np.linalg.norm(y))
+                print(f"[zero-mean smooth Q, FP8, causal={causal}] cos={c:.8f} maxabs={np.abs(x - y).max():.2e}")
+                assert c >= 0.99999, (causal, c)
 
 
 def test_attn_smooth_q_constant_q_rows_and_constant_k():

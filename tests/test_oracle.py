@@ -14,7 +14,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from exact_fp import (e4m3_round, e4m3_values, f32_bits, f32_from_bits, rn32, rn64, rne_int)
+from exact_fp import (e4m3_round, e4m3_values, f32_bits, f32_from_bits, rn32, rn64, rne_int, round_binary)
 from oracle import sage_oracle as O
 from quantized_attention_transformer_amd import synth
 
@@ -357,6 +357,68 @@ def test_fp8_oracle_close_to_fp16_oracle():
     # the V scale is per (sequence, head, channel) and maps the absmax to 448
     vd = O.e4m3_decode(qd["v8"][0, :, 0, :])
     assert np.abs(vd).max() == 448.0
+
+
+def _e4m3_exact(x: Fraction) -> Fraction:
+    """E4M3 rounding of a non-negative rational at most 448 (3 fraction bits,
+    smallest normal exponent -6), in exact arithmetic."""
+    r = round_binary(x, 3, -6, 8)
+    assert r <= 448
+    return r
+
+
+@pytest.mark.parametrize("scale", [0.5, 4.0, 40.0])
+def test_fp8_probs_codes_do_not_depend_on_key_order(scale):
+    """The reading of the FP8 scale of P (fp8_probs): P is taken relative to
+    the row maximum rounded up to an integer in base-2 units, so that a
+    kernel that visits the keys tile by tile, with a running maximum rounded
+    up the same way, reaches the same E4M3 weights as the two-pass oracle in
+    any visiting order: its shift to the final reference is a power of two,
+    which commutes with E4M3 rounding in the normal range.  Also pins max
+    448 p in (224, 448], and that the plain-maximum reading does not have the
+    property (so the choice stays visible)."""
+    rng = np.random.default_rng(int(scale * 10))
+    S = rng.standard_normal((6, 192)) * scale
+    P, l = O.fp8_probs(S)
+    x = S * O.LOG2E
+    top = 448.0 * P.max(axis=1)
+    assert (top > 224.0).all() and (top <= 448.0).all()
+    np.testing.assert_allclose(l[:, 0], P.sum(axis=1), rtol=1e-15)
+    mf = np.ceil(x.max(axis=1))
+    plain_mismatch = plain_total = 0
+    for i in range(S.shape[0]):
+        ref = [_e4m3_exact(448 * Fraction(float(p))) for p in P[i]]
+        normal = [448.0 * p >= 2.0 ** -6 for p in P[i]]
+        for trial in range(3):
+            keys = rng.permutation(S.shape[1])
+            tiles = [keys[t:t + 32] for t in range(0, len(keys), 32)]
+            m = -math.inf
+            got = {}
+            for tile in tiles:
+                m = max(m, math.ceil(x[i, tile].max()))
+                k = int(mf[i] - m)                 # integer shift to the final reference
+                for j in tile:
+                    # E4M3(448 * 2^(x_j - m)) with the oracle's p_j = 2^(x_j - m_final)
+                    got[j] = (_e4m3_exact(448 * Fraction(float(P[i, j])) * Fraction(2) ** k), m)
+            assert m == mf[i]                      # the running maximum ends at the same integer
+            for j, (code_val, mj) in got.items():
+                w = code_val * Fraction(2) ** int(mj - mf[i])
+                if normal[j]:
+                    assert w == ref[j], (i, j)
+            # the plain-maximum reading: running maxima are not integers, so
+            # the shifts are not powers of two and the weights move
+            xm = x[i].max()
+            M = -math.inf
+            for tile in tiles:
+                M = max(M, x[i, tile].max())
+                for j in tile:
+                    a = Fraction(float(448.0 * np.exp2(x[i, j] - M)))
+                    w = float(_e4m3_exact(min(a, Fraction(448)))) * 2.0 ** (M - xm)
+                    two_pass = float(_e4m3_exact(Fraction(float(448.0 * np.exp2(x[i, j] - xm)))))
+                    if two_pass >= 2.0 ** -6:          # compared in the normal range only
+                        plain_total += 1
+                        plain_mismatch += w != two_pass
+    assert plain_mismatch > 0.05 * plain_total
 
 
 # ---------------------------------------------------------------- smooth V (FP8 P.V path)
