@@ -233,6 +233,25 @@ int sage_attn(const sage_problem* p,
               int causal, float sm_scale, int pv_mode,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* sage_attn for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation as sage_attn (same kernels, same results), with the
+ * workspace taken from a fixed array of SAGE_NOALLOC_SCRATCH_BYTES bytes that
+ * the library holds on each GPU it runs on until the process ends (its
+ * device address is looked up on the entry's first call on a device; the
+ * entry calls no hipMalloc/hipFree and no allocating routine).  Problems
+ * whose sage_workspace_bytes exceed it are refused with SAGE_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads) race and must not be issued;
+ * calls in one stream are ordered.  The stream must belong to the current
+ * device.  Nothing in the array must start zeroed (every byte read is
+ * written earlier in the same call). */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sage_attn_noalloc(const sage_problem* p,
+                      const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                      const void* V, sage_strides vs, void* out, sage_strides os,
+                      int causal, float sm_scale, int pv_mode, void* stream);
+
 /* Debug: the INT32 scores S_int = q8 . k8^T of the fused kernel's integer
  * stage ("SageAttention：低比特量化Attention，实现推理加速", 技术方案 item 2:
  * INT8 product, INT32 accumulator), taken from the fused kernel itself: a

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "sage.h"
@@ -481,9 +482,10 @@ int sage_attn_quantized(const sage_problem* p, const int8_t* q8, sage_strides q8
   return SAGE_OK;
 }
 
-int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks, const void* V,
-              sage_strides vs, void* out, sage_strides os, int causal, float sm_scale, int pv_mode, void* workspace,
-              size_t workspace_bytes, void* stream) {
+// Arguments of sage_attn / sage_attn_noalloc checked; the workspace is the
+// caller's or the library's scratch array.
+static int check_attn_args(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                           const void* V, sage_strides vs, void* out, sage_strides os, int pv_mode) {
   int rc = check_problem(p, true);
   if (rc || (rc = fp4_head_dim(p))) return rc;
   if (!valid_pv_mode(pv_mode)) return fail(SAGE_ERR_INVALID_ARG, "bad pv_mode %d", pv_mode);
@@ -491,13 +493,31 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   if ((rc = check_tensor("Q", Q, qs, 8, p)) || (rc = check_tensor("K", K, ks, 8, p)) ||
       (rc = check_tensor("V", V, vs, 8, p)) || (rc = check_tensor("out", out, os, 8, p)))
     return rc;
-  if ((rc = check_row_span("V", vs, 2, p))) return rc;
+  return check_row_span("V", vs, 2, p);
+}
+
+static int run_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                    const void* V, sage_strides vs, void* out, sage_strides os, int causal, float sm_scale,
+                    int pv_mode, char* ws, hipStream_t st);
+
+int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks, const void* V,
+              sage_strides vs, void* out, sage_strides os, int causal, float sm_scale, int pv_mode, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int rc = check_attn_args(p, Q, qs, K, ks, V, vs, out, os, pv_mode);
+  if (rc || empty(p)) return rc;
   const WsLayout w = ws_layout(p, pv_mode);
   if (!workspace || workspace_bytes < w.total)
     return fail(SAGE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, w.total);
   if (!aligned16(workspace)) return fail(SAGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  char* ws = (char*)workspace;
-  hipStream_t st = (hipStream_t)stream;
+  return run_attn(p, Q, qs, K, ks, V, vs, out, os, causal, sm_scale, pv_mode, (char*)workspace,
+                  (hipStream_t)stream);
+}
+
+static int run_attn(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                    const void* V, sage_strides vs, void* out, sage_strides os, int causal, float sm_scale,
+                    int pv_mode, char* ws, hipStream_t st) {
+  int rc;
+  const WsLayout w = ws_layout(p, pv_mode);
   int8_t* q8 = (int8_t*)(ws + w.q8);
   int8_t* k8 = (int8_t*)(ws + w.k8);
   float* sq = (float*)(ws + w.sq);
@@ -542,6 +562,50 @@ int sage_attn(const sage_problem* p, const void* Q, sage_strides qs, const void*
   hipError_t e = sage::launch_attn(to_internal(p), a, causal != 0, pv_mode != SAGE_PV_FP16, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SAGE_OK;
+}
+
+// ---- sage_attn_noalloc: the workspace in a file-scope device array.  Its
+// name is a host-side stand-in, not a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device, fetched at the
+// entry's first call on that device and kept per device.
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+}  // namespace
+
+int sage_attn_noalloc(const sage_problem* p, const void* Q, sage_strides qs, const void* K, sage_strides ks,
+                      const void* V, sage_strides vs, void* out, sage_strides os, int causal, float sm_scale,
+                      int pv_mode, void* stream) {
+  int rc = check_attn_args(p, Q, qs, K, ks, V, vs, out, os, pv_mode);
+  if (rc || empty(p)) return rc;
+  const size_t need = ws_layout(p, pv_mode).total;
+  if (need > SAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(SAGE_ERR_WORKSPACE,
+                "sage_attn_noalloc: this problem needs %zu bytes of scratch, above the library's fixed %zu-byte "
+                "array (use sage_attn with a workspace)",
+                need, (size_t)SAGE_NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return run_attn(p, Q, qs, K, ks, V, vs, out, os, causal, sm_scale, pv_mode, ws, (hipStream_t)stream);
 }
 
 int sage_debug_qk_i32(const sage_problem* p, const int8_t* q8, sage_strides q8s, const int8_t* k8, sage_strides k8s,

@@ -29,7 +29,7 @@ EXPORTED = ("sage_workspace_bytes", "sage_quantize_workspace_bytes", "sage_quant
             "sage_quantize_v_fp8_smooth_workspace_bytes", "sage_quantize_v_fp8_smooth",
             "sage_quantize_smooth_q_workspace_bytes", "sage_quantize_smooth_q",
             "sage_quantize_mxfp4_workspace_bytes", "sage_quantize_mxfp4",
-            "sage_attn_quantized", "sage_attn", "sage_debug_qk_i32", "sage_debug_fp8_mfma",
+            "sage_attn_quantized", "sage_attn", "sage_attn_noalloc", "sage_debug_qk_i32", "sage_debug_fp8_mfma",
             "sage_debug_mxfp4_mfma", "sage_last_error")
 
 
@@ -71,6 +71,7 @@ def lib():
         L.sage_quantize_v_fp8_smooth.argtypes = [P, vp, S, vp, S, vp, vp, sz, vp]
         L.sage_attn_quantized.argtypes = [P, vp, S, vp, S, vp, vp, vp, S, vp, vp, S, i32, i32, vp]
         L.sage_attn.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp, sz, vp]
+        L.sage_attn_noalloc.argtypes = [P, vp, S, vp, S, vp, S, vp, S, i32, f32, i32, vp]
         L.sage_debug_qk_i32.argtypes = [P, vp, S, vp, S, vp, vp]
         L.sage_debug_fp8_mfma.argtypes = [vp, vp, vp, i32, i32, vp, vp]
         L.sage_debug_mxfp4_mfma.argtypes = [vp, vp, vp, vp, vp, vp, vp]
@@ -301,6 +302,25 @@ def attn(q, k, v, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAG
                          0.0 if sm_scale is None else float(sm_scale), pv_mode, _ptr(workspace),
                          workspace.numel(), _stream())
     _check("sage_attn", rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SAGE_NOALLOC_SCRATCH_BYTES
+
+
+def attn_noalloc(q, k, v, out, *, causal=False, sm_scale: Optional[float] = None, pv_mode=SAGE_PV_FP16,
+                 layout="bnhd", cu_seqlens=None, max_seqlen=None, blk_q=128, blk_k=64, smooth_q=False,
+                 qk_fp4=False):
+    """sage_attn_noalloc: sage_attn with the library's fixed scratch array as its
+    workspace (no device allocation by the library; `out` is the caller's).
+    Calls on one GPU share the array: they must not overlap."""
+    prob = make_problem(q, layout, cu_seqlens, max_seqlen, blk_q, blk_k, k=k)
+    prob.smooth_q = int(bool(smooth_q))
+    prob.qk_fp4 = int(bool(qk_fp4))
+    rc = lib().sage_attn_noalloc(ctypes.byref(prob), _ptr(q), strides_of(q, layout), _ptr(k), strides_of(k, layout),
+                                 _ptr(v), strides_of(v, layout), _ptr(out), strides_of(out, layout),
+                                 int(bool(causal)), 0.0 if sm_scale is None else float(sm_scale), pv_mode, _stream())
+    _check("sage_attn_noalloc", rc)
     return out
 
 
