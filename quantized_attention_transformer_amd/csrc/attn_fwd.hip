@@ -35,7 +35,8 @@
 // the same (lane half, k slot); V's operand is read to match:
 //   fp16: V stays row-major in LDS and ds_read_b64_tr_b16 transposes it on the
 //         read (two reads per operand);
-//   fp8:  V is written to LDS transposed ([channel][permuted key]).
+//   fp8:  V stays row-major in LDS too and ds_read_b64_tr_b8 transposes it
+//         (four reads per operand).
 //
 // Ping-pong schedule.  Time is cut into phases b = 0, 1, ..., ntiles+1, one
 // workgroup barrier after each.  In phase b the half with h = b mod 2 is in
@@ -43,11 +44,10 @@
 // is in its vector phase: the softmax of tile b-1.  So at any time one wave
 // of every SIMD feeds the matrix core while the other keeps the VALU busy,
 // and S and P need one register set each.  The half in its matrix phase b
-// also issues the loads of the tiles it will use next: V(b+2) and K(b+4) (K
-// straight into LDS with buffer_load ... lds; fp16 V too, E4M3 V through
-// registers so it can be transposed), and waits for them at the end of its
-// vector phase b+3, ~3.5 phases later.  K and V tiles live in rings of 5 LDS
-// slots.
+// also issues the loads of the tiles it will use next: V(b+2) and K(b+4),
+// straight into LDS with buffer_load ... lds, and waits for them at the end
+// of its vector phase b+3, ~3.5 phases later.  K and V tiles live in rings of
+// 5 LDS slots.
 //
 // Softmax.  The i32 accumulator starts at the bit pattern of 1.5*2^23, so the
 // MFMA leaves the float 1.5*2^23 + S exactly (|S| <= 127^2*128 < 2^22): no
@@ -80,6 +80,7 @@
 namespace sage {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -104,21 +105,24 @@ constexpr int NSK = 5;                  // K ring slots
 constexpr int NSV = 5;                  // V ring slots
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9 (raw, 32-bit format)
 
-// LDS of one workgroup.  K rows (D bytes) and fp16 V rows (2D bytes) are
-// stored without padding; 16-byte chunks are XOR-swizzled by row so that
-// every 256-byte LDS pass of the fragment reads (64 banks x 4 B) hits each
-// bank once:
-//   K:  chunk c of row r at c ^ ((r / (256/D)) % (D/16))   (ds_read_b128, 16 lanes = 16 rows)
-//   V:  chunk c of row r at c ^ 4*(r % 4)       (D = 128)  (ds_read_b64_tr_b16, 32 lanes =
-//                           c ^ 4*((r / 2) % 2) (D = 64)    4 rows x 64 bytes)
-// The E4M3 V is stored transposed ([channel][permuted key], rows of BN+16 bytes).
+// LDS of one workgroup.  K rows (D bytes), fp16 V rows (2D bytes) and E4M3
+// V rows (D bytes) are stored without padding, one key per row, straight from
+// the tile loads; 16-byte chunks are XOR-swizzled by row so that every
+// 256-byte LDS pass of the fragment reads (64 banks x 4 B) hits each bank
+// once:
+//   K:     chunk c of row r at c ^ ((r / (256/D)) % (D/16))   (ds_read_b128, 16 lanes = 16 rows)
+//   fp16 V: chunk c of row r at c ^ 4*(r % 4)       (D = 128)  (ds_read_b64_tr_b16, 32 lanes =
+//                              c ^ 4*((r / 2) % 2) (D = 64)    4 rows x 64 bytes)
+//   E4M3 V: chunk c of row r at c ^ (2*(r/2 % 2) + 4*(r/8 % 2))  (D = 128)  (ds_read_b64_tr_b8,
+//                              c ^ 2*(r/8 % 2)                  (D = 64)   32 lanes = 8 rows x
+//                                                                          32 bytes)
 // After the key loop the same bytes hold the second half's partial results.
 template <int D, bool FP8, bool QK4 = false>
 struct Lds {
   static constexpr int KROW = QK4 ? D / 2 : D;  // bytes of a K row (INT8, or MXFP4 codes)
   static constexpr int KBYTES = BN * KROW;
-  static constexpr int VROW = FP8 ? (BN + 16) : 2 * D;
-  static constexpr int VBYTES = (FP8 ? D : BN) * VROW;
+  static constexpr int VROW = FP8 ? D : 2 * D;
+  static constexpr int VBYTES = BN * VROW;
   static constexpr int VRING = NSK * KBYTES;  // offset of the V ring
   static constexpr int RING = VRING + NSV * VBYTES;
   static constexpr int MSTRIDE = D / 2 + 2;   // floats per lane of a partial result: O^T, m, l
@@ -139,14 +143,14 @@ struct Lds {
   static constexpr int DRING = BYTES;
   static constexpr int DBYTES = NSD * 1024;
   static constexpr int KCH = KBYTES / 1024;             // 1 KiB DMA blocks per K tile
-  static constexpr int VCH = FP8 ? 0 : VBYTES / 1024;   // (fp16 V)
+  static constexpr int VCH = VBYTES / 1024;            // 1 KiB DMA blocks per V tile
   __device__ static constexpr int kswz(int r) { return (r / (256 / KROW)) % (KROW / 16); }
-  __device__ static constexpr int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  __device__ static constexpr int vswz(int r) {
+    if constexpr (FP8) return D == 128 ? 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1) : 2 * ((r >> 3) & 1);
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
 };
 
-__device__ __forceinline__ int pos8(int kq) {  // byte position of key quad kq in an fp8 V^T row
-  return 32 * (kq & 1) + 16 * (kq >> 3) + 4 * ((kq & 7) >> 1);
-}
 
 // Buffer descriptor (gfx9 raw buffer): base, num_records bytes, stride 0.
 __device__ __forceinline__ v4i make_rsrc(const void* base, int bytes) {
@@ -184,7 +188,7 @@ template <int D, bool FP8, bool QK4 = false>
 struct DmaPlan {
   using S = Lds<D, FP8, QK4>;
   static constexpr int KPW = S::KCH / NWH;  // K blocks per wave
-  static constexpr int VPW = S::VCH / NWH;  // fp16 V blocks per wave
+  static constexpr int VPW = S::VCH / NWH;  // V blocks per wave
   static_assert(S::KCH % NWH == 0 && S::VCH % NWH == 0, "tile blocks split over a half");
   int koff[KPW];
   int voff[VPW > 0 ? VPW : 1];
@@ -200,7 +204,7 @@ struct DmaPlan {
 #pragma unroll
     for (int x = 0; x < VPW; ++x) {
       const int byte = (w + NWH * x) * 1024 + 16 * lane;
-      const int r = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ S::vswz(r);
+      const int r = byte / S::VROW, c = ((byte % S::VROW) / 16) ^ S::vswz(r);
       voff[x] = (int)(r * vn) + 16 * c;
     }
   }
@@ -224,60 +228,6 @@ struct DmaPlan {
     if constexpr (VPW > 0) {
 #pragma unroll
       for (int x = 0; x < VPW; ++x) dma_b128(vr, voff[x], lds_addr(slot + (w + NWH * x) * 1024));
-    }
-  }
-};
-
-// E4M3 V tile through registers: 4 keys x 8 channels per item, written to LDS
-// transposed.  Rows past the sequence are clamped to its last row.
-template <int D>
-struct V8Stager {
-  static constexpr int NTH = NWH * 64;  // threads of one half
-  static constexpr int VITEMS = (BN / 4) * (D / 8);
-  static constexpr int VPT = (VITEMS + NTH - 1) / NTH;
-  uint2 v8[VPT * 4];
-  __device__ __forceinline__ void load(const uint8_t* vseq, int64_t vn, int j0, int L, int tid) {
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vseq, 0, (int)((L - 1) * vn + D), kRsrcWord3);
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int idx = tid + x * NTH;
-      const int kq = idx % (BN / 4), cg = idx / (BN / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = min(j0 + 4 * kq + e, L - 1);
-        if (VITEMS % NTH == 0 || idx < VITEMS)
-          v8[x * 4 + e] =
-              __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, (int)(row * vn) + 8 * cg, 0, 0));
-      }
-    }
-  }
-  __device__ __forceinline__ void store(lds_u8* vl, int tid) const {
-    constexpr int VROW = Lds<D, true>::VROW;
-#pragma unroll
-    for (int x = 0; x < VPT; ++x) {
-      const int idx = tid + x * NTH;
-      const int kq = idx % (BN / 4), cg = idx / (BN / 4);
-      if (VITEMS % NTH == 0 || idx < VITEMS) {
-        const int pos = pos8(kq);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint32_t r0 = hf ? v8[x * 4 + 0].y : v8[x * 4 + 0].x;
-          const uint32_t r1 = hf ? v8[x * 4 + 1].y : v8[x * 4 + 1].x;
-          const uint32_t r2 = hf ? v8[x * 4 + 2].y : v8[x * 4 + 2].x;
-          const uint32_t r3 = hf ? v8[x * 4 + 3].y : v8[x * 4 + 3].x;
-          // byte b of the four key rows -> one dword per channel
-          const uint32_t lo01 = __builtin_amdgcn_perm(r1, r0, 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
-          const uint32_t hi01 = __builtin_amdgcn_perm(r1, r0, 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
-          const uint32_t lo23 = __builtin_amdgcn_perm(r3, r2, 0x05010400u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(r3, r2, 0x07030602u);
-          lds_u8* row = vl + (8 * cg + 4 * hf) * VROW + pos;
-          *(LDS uint32_t*)(row) = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-          *(LDS uint32_t*)(row + VROW) = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-          *(LDS uint32_t*)(row + 2 * VROW) = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-          *(LDS uint32_t*)(row + 3 * VROW) = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-        }
-      }
     }
   }
 };
@@ -407,7 +357,6 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   uint32_t kofs[D / 32];
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) kofs[kk] = li * S::KROW + 16 * ((2 * kk + g) ^ S::kswz(li));
-  const uint32_t vrow8 = li * S::VROW + 32 * g;  // FP8: this lane's V^T row and half
   // ... and the transposed fp16 V reads: rows 4g + tl/4 (+8), chunk 4ct + 2(b&1) + (tl&3)/2
   const int vb = lane >> 4, tl = lane & 15;
   int vaddr[D / 32];
@@ -416,12 +365,25 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     const int vr = 4 * g + (tl >> 2);
     vaddr[ct] = vr * S::VROW + 16 * ((4 * ct + 2 * (vb & 1) + ((tl & 3) >> 1)) ^ S::vswz(vr)) + 8 * (tl & 1);
   }
+  // ... and the transposed E4M3 V reads (ds_read_b64_tr_b8: in each group of 16
+  // lanes, lane t receives byte t%8 of the 8 bytes named by lanes t/8, t/8+2,
+  // .., t/8+14).  Lanes 2k and 2k+1 of a group name the two 8-channel halves
+  // of 16-channel chunk 2ct + (group%2) in key row k of the P.V contraction's
+  // slot order (rows 8(k/4) + 4g + k%4 of each 16 keys), so lane (m, g) gets 8
+  // keys of channel 32ct + m, in the order P holds them.
+  uint32_t vaddr8[D / 32];
+  {
+    const int t = lane & 15, k = t >> 1;
+    const int vr = 8 * (k >> 2) + 4 * g + (k & 3);
+    const int fh = S::vswz(vr) >> 1;  // (the swizzle of row 16 rr + vr is that of vr)
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct) vaddr8[ct] = vr * S::VROW + 16 * ((lane >> 4) & 1) + 8 * (t & 1) + 32 * (ct ^ fh);
+  }
 
   const bool ks_in_lds = KSU && !QK4 && !DUMP && ntiles <= S::KSCAP;
 
   DmaPlan<D, FP8, QK4> dma;
   dma.init(w & 3, lane, kn, vn);  // the plan covers a tile with the 4 waves of one half
-  V8Stager<D> v8s;
 
   float m = -INFINITY, lsum = 0.0f;
   // FP8: O and l accumulate relative to the first tile's maximum m0; tile t's
@@ -436,6 +398,15 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   v8h pf[4];    // fp16 P (between the vector phase and the next matrix phase)
   v8i pf8 = {};  // E4M3 P
 
+  // E4M3 V^T operand of channels 32ct .. 32ct+31 of the tile at LDS byte
+  // offset vso: four transposed reads of 8 keys (16 keys apart in the tile)
+  auto vread8 = [&](uint32_t vso, int ct) {
+    v2i r[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      r[rr] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS v2i*)(lds + vso + vaddr8[ct] + 16 * rr * S::VROW));
+    return v8i{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+  };
   // O^T += V^T . P^T for the tile at LDS byte offset vso
   auto pv = [&](uint32_t vso) {
     if constexpr (!FP8) {
@@ -454,15 +425,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         }
       }
     } else {
-      const lds_u8* vl = lds + (vso + vrow8);  // V^T rows = channels
 #pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) {
-        const lds_u8* pa = vl + 32 * ct * S::VROW;
-        const v4i va = *(const LDS v4i*)(pa);
-        const v4i vb2 = *(const LDS v4i*)(pa + 16);
-        const v8i vf = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf8, o[ct], 0, 0, 0, 127, 0, pscale);
-      }
+      for (int ct = 0; ct < D / 32; ++ct)
+        o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread8(vso, ct), pf8, o[ct], 0, 0, 0, 127, 0, pscale);
     }
   };
 
@@ -735,13 +700,13 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   // phase t+2), and waits for both at the end of its vector phase t-1, with
   // the loads of its matrix phase t-2 still in flight: ~3.5 phases of latency
   // hidden.  The barrier after that publishes them for the matrix phases t
-  // (K) and t+2 (V), run by the same half.  fp16: K and V straight to LDS;
-  // FP8: K to LDS, V to registers, stored transposed at the end of phase t-1.
+  // (K) and t+2 (V), run by the same half.  K and V go straight to LDS.
   // Descriptors of this half's next K and V tiles: base at the tile's first
   // row, size up to the sequence's end.
   const int8_t* knext = kseq + (int64_t)hf * BN * kn;
   const uint8_t* vnext = vseq + (int64_t)hf * BN * vn;
-  // (fp16 V rows hold dv channels: the last row is read up to them only)
+  // (fp16 V rows hold dv channels: the last row is read up to them only; E4M3
+  // V rows are the pre-pass's, of D channels)
   int krec = (int)((L - 1 - hf * BN) * kn + S::KROW);
   int vrec = DUMP ? -(1 << 30) : (int)((L - 1 - hf * BN) * vn + (FP8 ? D : 2 * p.dv));
   const int kstep = (int)(2 * BN * kn), vstep = (int)(2 * BN * vn);
@@ -754,16 +719,15 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   int ksrec = (L - hf * BN) * 4;
   const int ksstep = QK4 ? (int)(2 * BN * a.kss4.n) : 0;
   const int wh = w & 3, tidh = tid & (NWH * 64 - 1);  // wave and thread within the half
-  constexpr int KL = DmaPlan<D, FP8, QK4>::KPW, VL = FP8 ? 0 : DmaPlan<D, FP8, QK4>::VPW;
+  constexpr int KL = DmaPlan<D, FP8, QK4>::KPW, VL = DmaPlan<D, FP8, QK4>::VPW;
   constexpr int NOPS = KL + VL + (SQ ? 1 : 0) + (QK4 ? 1 : 0);  // DMA loads per wave per matrix phase
   constexpr int QKM = 2 * (QK4 ? D / 64 : D / 32);              // Q.K^T MFMAs per tile
-  // Every matrix phase issues NOPS DMA loads per wave (fp16: VL for V, then KL
-  // for K, then (smooth Q) one for the compensations; FP8: its V loads to
-  // registers come first, then the K and compensation loads).  At the end of a
+  // Every matrix phase issues NOPS DMA loads per wave: VL for V, then KL for
+  // K, then (smooth Q, 4-bit) one for the per-key words.  At the end of a
   // vector phase the loads of the previous matrix phase may stay in flight:
-  // s_waitcnt vmcnt(NOPS) (FP8: vmcnt(KL (+1)), its V registers are needed now).
+  // s_waitcnt vmcnt(NOPS).
   auto wait_older = [&] {
-    constexpr int n = FP8 ? KL + (SQ ? 1 : 0) + (QK4 ? 1 : 0) : NOPS;
+    constexpr int n = NOPS;
     static_assert(n >= 1 && n <= 7, "wait counts below");
     if constexpr (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else if constexpr (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
@@ -774,15 +738,15 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
   };
 
-  // ---- prologue.  With a partial last tile the fp16 V ring starts zeroed:
-  // the rows of that tile past the sequence are never loaded, and their
-  // (masked, P = 0) keys must still meet finite V.  Everything else a masked
-  // key reads may be anything: K codes are finite by construction, the E4M3 V
-  // goes through registers with its rows clamped to the sequence, and scores
-  // of masked keys are replaced, not scaled.  Then, in one batch of loads in
+  // ---- prologue.  With a partial last tile the V ring starts zeroed: the
+  // rows of that tile past the sequence are never loaded, and their (masked,
+  // P = 0) keys must still meet finite V (fp16, or an E4M3 code that is not
+  // NaN; later tiles leave codes of the pre-pass there, all finite).
+  // Everything else a masked key reads may be anything: K codes are finite
+  // by construction, and scores of masked keys are replaced, not scaled.  Then, in one batch of loads in
   // flight together with the Q fragments: half h's tiles K(h), K(h+2) and V(h)
   // (empty descriptors past the end) and the per-tile k_scale table.
-  if (!FP8 && (L % BN) != 0) {
+  if ((L % BN) != 0) {
     for (int x = tid; x < NSV * S::VBYTES / 16; x += NT) *(LDS v4i*)(lds + S::VRING + 16 * x) = v4i{0, 0, 0, 0};
     // The zeroes are in place before any tile lands: this wave's LDS stores
     // are complete, then the barrier (the branch is the same for the whole
@@ -800,10 +764,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         const int t = tid + j * NT;
         ksv[j] = t < ntiles ? keff(ksc[(t * BN) / p.blk_k]) : 0.0f;
       }
-    if constexpr (FP8)
-      v8s.load(vseq, vn, hf * BN, L, tidh);
-    else
-      dma.issue_v(make_rsrc(vnext, max(vrec, 0)), lds + voff(hf), wh);
+    dma.issue_v(make_rsrc(vnext, max(vrec, 0)), lds + voff(hf), wh);
     vnext += vstep;
     vrec -= vstep;
     dma.issue_k(make_rsrc(knext, max(krec, 0)), lds + koff(hf), wh);
@@ -823,7 +784,6 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       ksrec -= 2 * dstep;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (FP8) v8s.store(lds + voff(hf), tidh);
     if (ks_in_lds)
 #pragma unroll
       for (int j = 0; j < KSPT; ++j) {
@@ -856,7 +816,6 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // K(b+1) and V(b-1) must have landed; in flight from matrix phase b-1
       // may stay: V(b+1), then K(b+3)
       wait_older();
-      if constexpr (FP8) v8s.store(lds + voff(wrap(ph + 1)), tidh);  // V(b+1), from registers
     }
     // nothing moves across the phase boundary (the other half's work of the
     // next phase must not start in this one)
@@ -964,15 +923,9 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      const lds_u8* vl = lds + (vso + vrow8);  // V^T rows = channels
       v8i vf[D / 32];
 #pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) {
-        const lds_u8* pa = vl + 32 * ct * S::VROW;
-        const v4i va = *(const LDS v4i*)(pa);
-        const v4i vb2 = *(const LDS v4i*)(pa + 16);
-        vf[ct] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int ct = 0; ct < D / 32; ++ct) vf[ct] = vread8(vso, ct);
       __builtin_amdgcn_sched_barrier(0);
       qk_mfmas();
 #pragma unroll
@@ -1004,7 +957,6 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       ksr = make_rsrc(ksnext, max(ksrec, 0));
       kssl = lds + ksoffs(wrap6(pd + 4));  // K's E8M0 words of tile b+4, with K(b+4)
     }
-    if constexpr (FP8) v8s.load(vseq, vn, (b + 2) * BN, L, tidh);
     auto op = [&](int x) {
       if (x < VL)
         dma.issue_v1(vr, vsl, wh, x);
