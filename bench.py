@@ -280,6 +280,7 @@ EXTRA_CASES = [
     ("sage_attn 4-bit QK (MXFP4) fp16-PV B4 H16 N8192 d128", "FP8", False, 0, "fp4"),
     ("sage_attn 4-bit QK (MXFP4) FP8-PV B4 H16 N8192 d128", "FP8", False, 1, "fp4"),
     ("sage_quantize long B1 H32 N32768 d128", "LONG", False, 0, "prepass"),
+    ("sage_quantize text B1 H8 N4096 d128", "TEXT", False, 0, "prepass"),
 ]
 
 
@@ -315,11 +316,29 @@ def prepare_case(sage, torch, inputs, name, wl_name, causal, mode, kind):
     kw = {} if cu is None else dict(cu_seqlens=cu, max_seqlen=max(seqlens))
     H, d = q.shape[-2], q.shape[-1]
     if kind == "prepass":
+        # sage_quantize through the C ABI on preallocated outputs (int8 Q and K
+        # in the head-major layout sage_attn's workspace uses)
+        import ctypes
+        L = sage.lib()
         prob = sage.make_problem(q, blk_q=wl.blk_q, blk_k=wl.blk_k, k=k, **kw)
+        B, N, Hq, d = q.shape if q.dim() == 4 else (1, q.shape[0], q.shape[1], q.shape[2])
+        q8 = torch.empty((B, Hq, N, d), dtype=torch.int8, device=q.device)
+        k8 = torch.empty((B, k.shape[-2], N, d), dtype=torch.int8, device=q.device)
+        sq = torch.empty((len(seqlens), Hq, -(-max(seqlens) // wl.blk_q)), dtype=torch.float32, device=q.device)
+        sk = torch.empty((len(seqlens), k.shape[-2], -(-max(seqlens) // wl.blk_k)), dtype=torch.float32,
+                         device=q.device)
+        km = torch.empty((len(seqlens), k.shape[-2], d), dtype=torch.float32, device=q.device)
         ws = torch.empty(max(16, sage.quantize_workspace_bytes(prob)), dtype=torch.uint8, device=q.device)
+        s_in, s8 = sage.strides_of(q, "bnhd"), sage.strides_of(q8, "bhnd")
+        s8k = sage.strides_of(k8, "bhnd")
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        P = ctypes.byref(prob)
 
         def run():
-            sage.quantize(q, k, blk_q=wl.blk_q, blk_k=wl.blk_k, workspace=ws, **kw)
+            rc = L.sage_quantize(P, q.data_ptr(), s_in, k.data_ptr(), sage.strides_of(k, "bnhd"), 0.0, q8.data_ptr(),
+                                 s8, k8.data_ptr(), s8k, sq.data_ptr(), sk.data_ptr(), km.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), sp)
+            assert rc == 0, L.sage_last_error()
         ntok = sum(seqlens)
         nbq = sum(-(-L // wl.blk_q) for L in seqlens)
         nbk = sum(-(-L // wl.blk_k) for L in seqlens)

@@ -397,6 +397,10 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   v16i sc[2];   // S of the tile between its matrix and vector phases
   v8h pf[4];    // fp16 P (between the vector phase and the next matrix phase)
   v8i pf8 = {};  // E4M3 P
+  // FP8: the tile's fp32 P, from its softmax (vector phase) to the next matrix
+  // phase, which packs it to E4M3 and adds it into l in the shadow of its
+  // Q.K^T MFMAs (the vector phase is the longer one on this path)
+  float pr8[FP8 ? 32 : 1];
 
   // E4M3 V^T operand of channels 32ct .. 32ct+31 of the tile at LDS byte
   // offset vso: four transposed reads of 8 keys (16 keys apart in the tile)
@@ -558,7 +562,13 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         }
       mt = xhalf_max(mx);
     }
-    float alpha;
+    // O and l move to a new reference only in a rare, wave-uniform branch
+    // (its test is the only work the common case does for it)
+    auto rescale = [&](float alpha) {
+      lsum *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
+    };
     if constexpr (FP8) {
       // integer running maximum; the first finite one becomes the reference m0
       mt = ceilf(mt);
@@ -566,9 +576,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       m = fmaxf(m, mt);
       // O keeps the reference m0 unless m runs more than 100 past it; then O
       // and l move to the new reference m0 = m.
-      const float mn0 = (m - m0 > 100.0f) ? m : m0;
-      alpha = mn0 == m0 ? 1.0f : __builtin_amdgcn_exp2f(m0 - mn0);
-      m0 = mn0;
+      if (__builtin_expect(__any(m - m0 > 100.0f), 0)) {
+        const float mn0 = (m - m0 > 100.0f) ? m : m0;
+        rescale(mn0 == m0 ? 1.0f : __builtin_amdgcn_exp2f(m0 - mn0));
+        m0 = mn0;
+      }
       pscale = 127 + (int)(m - m0);
     } else {
       // lazy running maximum: a row moves its reference m only when the tile
@@ -576,14 +588,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       // far from overflow)
       // (kept an integer: with c below 1 the bias below is then exact, and
       // every rescale factor 2^(m_old - m_new) is a power of two)
-      const float mn = mt > m + 8.0f ? ceilf(mt) : m;
-      alpha = mn == m ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-    }
-    if (__builtin_expect(__any(alpha != 1.0f), 0)) {
-      lsum *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) o[ct] *= alpha;
+      if (__builtin_expect(__any(mt > m + 8.0f), 0)) {
+        const float mn = mt > m + 8.0f ? ceilf(mt) : m;
+        rescale(mn == m ? 1.0f : __builtin_amdgcn_exp2f(m - mn));
+        m = mn;
+      }
     }
     const float mref = FP8 ? m - kLog2_448 : m;  // FP8: P scaled by 448 inside the exponent
     // Exponent x c - (MAG c + mref), one FMA per score.  The FMA rounds once,
@@ -594,12 +603,12 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     // 1 that unit divides m too and the sum stays below 2^24 of them (|m| <=
     // 2^21 c + 9), so the bias is exact (for c below 2^-18, where m is the
     // larger term, it is rounded at the size of m only).  FP8: mref = m -
-    // log2(448) is not an
-    // integer; the bias is rounded up (by at least its rounding error), so
-    // 448 P never exceeds 448, and its error, at most an ulp of MAG c, stays
-    // below 2^-10 log2 units while c < 2^-9 (scores of unit-scale Q and K
-    // have c ~ 2^-12).  Larger c (any lane) take the slow form: the seed
-    // subtracted first, exactly, one more instruction per score.
+    // log2(448) is not an integer; the bias is rounded up (by at least its
+    // rounding error), so 448 P never exceeds 448, and its error, at most an
+    // ulp of MAG c, stays below 2^-10 log2 units while c < 2^-9 (scores of
+    // unit-scale Q and K have c ~ 2^-12).  Larger c (any lane) take the slow
+    // form: the seed subtracted first, exactly, one more instruction per
+    // score.
     bool slow = false;
     if constexpr (BIASED) slow = __builtin_expect(__any(c[0][0] >= (FP8 ? 0x1p-9f : 1.0f)), 0);
     float bias = __builtin_fmaf(MAG, c[0][0], mref);
@@ -657,31 +666,36 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       }
       asm volatile("" : "+v"(lsum));
     } else {
-      float ps = 0.0f;
       auto emit = [&](auto slow_tag) {
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 16; r += 4) {
-            const float p0 = prob(jt, r, slow_tag), p1 = prob(jt, r + 1, slow_tag), p2 = prob(jt, r + 2, slow_tag),
-                        p3 = prob(jt, r + 3, slow_tag);
-            ps = (jt == 0 && r == 0) ? (p0 + p1) + (p2 + p3) : ps + ((p0 + p1) + (p2 + p3));
-            // (the conversion writes one half of the word and keeps the other:
-            // the previous tile's bits stand in for the half written next)
-            uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (uint32_t)pf8[4 * jt + r / 4], false);
-            wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
-            pf8[4 * jt + r / 4] = (int)wv;
-          }
+          for (int r = 0; r < 16; ++r) pr8[16 * jt + r] = prob(jt, r, slow_tag);
       };
       if (BIASED && slow)
         emit(std::true_type{});
       else
         emit(std::false_type{});
-      lsum += __builtin_ldexpf(ps, pscale - 127);
-      asm volatile("" : "+v"(pf8));
-      asm volatile("" : "+v"(lsum));
+      // P is complete here, in this (vector) phase
+#pragma unroll
+      for (int j = 0; j < 32; ++j) asm volatile("" : "+v"(pr8[j]));
     }
   };
+  // FP8: E4M3 P for the P.V MFMA and l += sum of P (relative to m0, at this
+  // tile's scale 2^(pscale - 127)), in 8 pieces of 4 keys (word w of pf8),
+  // spread over the matrix phase's Q.K^T MFMAs; fin() adds the sum to l.
+  float ps8[4];
+  auto pack8 = [&](int w) {
+    const float p0 = pr8[4 * w], p1 = pr8[4 * w + 1], p2 = pr8[4 * w + 2], p3 = pr8[4 * w + 3];
+    // (the conversion writes one half of the word and keeps the other: the
+    // previous tile's bits stand in for the half written next)
+    uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (uint32_t)pf8[w], false);
+    wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
+    pf8[w] = (int)wv;
+    const float q = (p0 + p1) + (p2 + p3);
+    ps8[w & 3] = w < 4 ? q : ps8[w & 3] + q;
+  };
+  auto pack8_fin = [&] { lsum += __builtin_ldexpf((ps8[0] + ps8[1]) + (ps8[2] + ps8[3]), pscale - 127); };
 
   // Ring slots: tile t lives in K slot t % NSK and V slot t % NSV (NSK = NSV =
   // 5); ph = b % 5 is advanced at the end of every phase.
@@ -722,6 +736,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   constexpr int KL = DmaPlan<D, FP8, QK4>::KPW, VL = DmaPlan<D, FP8, QK4>::VPW;
   constexpr int NOPS = KL + VL + (SQ ? 1 : 0) + (QK4 ? 1 : 0);  // DMA loads per wave per matrix phase
   constexpr int QKM = 2 * (QK4 ? D / 64 : D / 32);              // Q.K^T MFMAs per tile
+  static_assert(8 % QKM == 0, "FP8 packing pieces per Q.K^T MFMA");
   // Every matrix phase issues NOPS DMA loads per wave: VL for V, then KL for
   // K, then (smooth Q, 4-bit) one for the per-key words.  At the end of a
   // vector phase the loads of the previous matrix phase may stay in flight:
@@ -864,6 +879,13 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
         for (int kk = 0; kk < D / 64; ++kk) ksb[jt][kk] = (int)((wk >> (8 * (2 * kk + g))) & 0xFFu);
       }
     }
+    // FP8: the previous tile's P packed and summed, 8 / QKM pieces per Q.K^T MFMA
+    auto fill = [&](int x) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int y = 0; y < 8 / QKM; ++y) pack8(x * (8 / QKM) + y);
+      }
+    };
     // (sched_barrier(0): the instruction order below is the schedule)
     auto qk_mfmas = [&] {
 #pragma unroll
@@ -876,6 +898,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
             const v8i qb = __builtin_shufflevector(qf[kk], qf[kk], 0, 1, 2, 3, 4, 5, 6, 7);
             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qb, acc, 4, 4, 0, ksb[jt][kk], 0, qsb[kk]);
             if (jt * KK + kk < NOPS) op(jt * KK + kk);
+            fill(jt * KK + kk);
             __builtin_amdgcn_sched_barrier(0);
           }
           sc[jt] = __builtin_bit_cast(v16i, acc);
@@ -885,6 +908,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
           for (int kk = 0; kk < KK; ++kk) {
             acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[jt][kk], qf[kk], acc, 0, 0, 0);
             if (jt * KK + kk < NOPS) op(jt * KK + kk);
+            fill(jt * KK + kk);
             __builtin_amdgcn_sched_barrier(0);
           }
           sc[jt] = acc;
@@ -928,6 +952,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
       for (int ct = 0; ct < D / 32; ++ct) vf[ct] = vread8(vso, ct);
       __builtin_amdgcn_sched_barrier(0);
       qk_mfmas();
+      pack8_fin();
 #pragma unroll
       for (int ct = 0; ct < D / 32; ++ct) {
         o[ct] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[ct], pf8, o[ct], 0, 0, 0, 127, 0, pscale);
@@ -972,7 +997,14 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
     } else {
 #pragma unroll
       for (int x = 0; x < NOPS; ++x) op(x);
-      if (b >= 2 && b - 2 < wtiles) pv(voff(wrap(ph + 3)));
+      if (b >= 2 && b - 2 < wtiles) {
+        if constexpr (FP8) {
+#pragma unroll
+          for (int w8 = 0; w8 < 8; ++w8) pack8(w8);
+          pack8_fin();
+        }
+        pv(voff(wrap(ph + 3)));
+      }
       if (b < wtiles) {
         if constexpr (QK4)
           qk4_tile(koff(ph), ksoffs(pd));

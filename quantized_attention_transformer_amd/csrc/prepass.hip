@@ -267,20 +267,23 @@ __device__ __forceinline__ void colsum_chunk(const _Float16* __restrict__ base, 
   }
 }
 
-// grid (nqw + nks, heads, nseq), kQThreads (heads: of Q).  Workgroups x < nqw quantise Q
-// (INT8 Q' = Q * sm_scale): block x of blk_q rows, or for blk_q == 1 (one
-// scale per token) the RPP rows x*RPP .. x*RPP+RPP-1, TPR threads per row.
-// Workgroups x >= nqw with a K head (y < kv_heads) take the fp64 column sums
-// of K over the tokens of chunk x - nqw (kKChunkRows tokens), one partial per
-// chunk.
+// grid (nkc + nqw, heads, nseq), kQThreads (heads: of Q).  Workgroups x < nkc
+// with a K head (y < kv_heads) take the fp64 column sums of K over the tokens
+// of chunk x (kKChunkRows tokens), one partial per chunk -- the longest work,
+// dispatched first.  Workgroups x >= nkc quantise Q (INT8 Q' = Q * sm_scale):
+// block x - nkc of blk_q rows, or for blk_q == 1 (one scale per token) the RPP
+// rows (x - nkc)*RPP .. + RPP - 1, TPR threads per row.
 template <int D>
 __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
     const _Float16* __restrict__ Q, Str qs, const _Float16* __restrict__ K, Str ks, const int32_t* __restrict__ cu,
-    int max_seqlen, int total, int blk_q, int nbq, int nqw, int nks, int kv_heads, int dv, float sm_scale,
+    int max_seqlen, int total, int blk_q, int nbq, int nkc, int nks, int kv_heads, int dv, float sm_scale,
     int8_t* __restrict__ q8, Str q8s,
     float* __restrict__ sq, double* __restrict__ part) {
   constexpr int TPR = D / 8, RPP = kQThreads / TPR;
-  const int x = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  const int h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  // x < nqw: Q work; x >= nqw: K chunk x - nqw (dispatched first: blockIdx.x < nkc)
+  const int nqw = gridDim.x - nkc;
+  const int x = (int)blockIdx.x < nkc ? nqw + (int)blockIdx.x : (int)blockIdx.x - nkc;
   const int L = seq_len(cu, s, max_seqlen, total);
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const bool cgv = 8 * cg < dv;  // this thread's 8 channels are real (not head_dim 96 padding)
@@ -514,7 +517,10 @@ __global__ __launch_bounds__(kQThreads) void k_quant_k(const _Float16* __restric
                                                        float* __restrict__ km, int8_t* __restrict__ k8, Str k8s,
                                                        float* __restrict__ sk) {
   constexpr int TPR = D / 8;
-  const int bi = blockIdx.x, h = blockIdx.y, s = blockIdx.z, H = gridDim.y;
+  // heads and sequences in the reverse of k_quant_q_colsum's order: the K rows
+  // that pass read last are read again first, while the memory-side cache may
+  // still hold them
+  const int bi = blockIdx.x, H = gridDim.y, h = H - 1 - blockIdx.y, s = gridDim.z - 1 - blockIdx.z;
   const int L = seq_len(cu, s, max_seqlen, total);
   const int n0 = bi * blk_k;
   if (n0 >= L) return;
@@ -831,8 +837,8 @@ hipError_t launch_quant_q_colsum(const Problem& p, const void* Q, Str qs, const 
     constexpr int RPP = kQThreads / (D / 8);  // rows per workgroup of the per-token path
     const int nqw = p.blk_q == 1 ? (p.max_seqlen + RPP - 1) / RPP : p.nbq;
     const int nkc = (p.max_seqlen + kKChunkRows - 1) / kKChunkRows;  // K column-sum chunks per head
-    hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nqw + nkc, p.heads, p.nseq), dim3(kQThreads), 0, st,
-                       (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.blk_q, p.nbq, nqw,
+    hipLaunchKernelGGL((k_quant_q_colsum<D>), dim3(nkc + nqw, p.heads, p.nseq), dim3(kQThreads), 0, st,
+                       (const _Float16*)Q, qs, (const _Float16*)K, ks, p.cu, p.max_seqlen, p.total, p.blk_q, p.nbq, nkc,
                        p.nks, p.kv_heads, p.dv, sm_scale, q8, q8s, q_scale, partial);
   });
   return hipGetLastError();
