@@ -31,10 +31,22 @@ namespace {
 
 constexpr int kThreads = 256;  // E4M3 V kernels
 
+// Cross-lane moves without LDS: DPP within a row of 16 lanes, then gfx950's
+// row swaps (permlane16/32_swap).  A chain of LDS permutes instead costs an
+// LDS round trip per step.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));   // lane i^1 (quad_perm [1,0,3,2])
+  v = fmaxf(v, dpp_f<0x4E>(v));   // lane i^2 (quad_perm [2,3,0,1])
+  v = fmaxf(v, dpp_f<0x141>(v));  // lane 7-i of its 8 (row_half_mirror): max over 8
+  v = fmaxf(v, dpp_f<0x140>(v));  // lane 15-i of its 16 (row_mirror): max over the row
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));  // rows 0|1, 2|3
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));  // halves
 }
 
 // Block-wide max of a non-negative value (NTH threads).
@@ -288,7 +300,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_q_colsum(
   const int tid = threadIdx.x, cg = tid % TPR, r = tid / TPR;
   const bool cgv = 8 * cg < dv;  // this thread's 8 channels are real (not head_dim 96 padding)
   const int64_t sh = (int64_t)s * H + h;
-  auto scale_q = [&](float v, int) { return v * sm_scale; };
+  // fp32(Q * sm_scale), one rounding of the exact product (as an FMA with a
+  // zero addend the fp16 operand is read directly: v_fma_mix_f32)
+  auto scale_q = [&](float v, int) { return __builtin_fmaf(v, sm_scale, 0.0f); };
   if (x < nqw && blk_q == 1) {
     // one scale per token: absmax of the row = fp32(max |Q| * sm_scale) (monotone)
     if (x * RPP >= L) return;
