@@ -519,6 +519,32 @@ def test_per_token_q_scales():
     assert cos(o1, ref) > cos(o64, ref)
 
 
+def test_k_granularity_finer_than_16_tokens_gains_little():
+    """How fine K's scales need to be ([SA2] 技术方案 item 2 argues for
+    granularities finer than per block).  On the text and video recipes
+    (smoothed K), against exact attention: K blocks of 64 -> 16 tokens and 16
+    -> 1 token each lower the RMS error by under 12%, while one Q scale per
+    token (128 -> 1) lowers it by more than K's step to single tokens does.
+    Smoothing has already taken the per-channel offset out of K; what a
+    finer K scale removes is the spread of row magnitudes, which is small
+    for keys.  So the library stops K at blocks of 16 tokens and offers
+    per-token scales for Q."""
+    from quantized_attention_transformer_amd import synth
+    for wl in (synth.TEXT, synth.VIDEO):
+        inp = synth.generate(wl, seqlen=1024, batch=1, heads=2)
+        ex = O.exact_attention(inp.q, inp.k, inp.v, inp.seqlens, None, False)
+
+        def rms(bq, bk):
+            o, _ = O.sage_attn(inp.q, inp.k, inp.v, inp.seqlens, None, False, bq, bk)
+            return float(np.sqrt(((o - ex) ** 2).mean()))
+        e64, e16, e1 = rms(128, 64), rms(128, 16), rms(128, 1)
+        eq1 = rms(1, 64)
+        print(f"[{wl.name}] rms: K blocks 64 {e64:.3e}, 16 {e16:.3e}, 1 {e1:.3e}; per-token Q {eq1:.3e}")
+        assert e1 <= e16 <= e64 * 1.001
+        assert 1 - e16 / e64 < 0.12 and 1 - e1 / e16 < 0.12
+        assert 1 - eq1 / e64 > 1 - e1 / e16
+
+
 # ---------------------------------------------------------------- grouped-query attention
 
 @pytest.mark.parametrize("hk", [1, 2])
