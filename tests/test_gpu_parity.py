@@ -238,8 +238,12 @@ def test_attn_small_full_compare(name, wl, kw, causal, bq, bk, fp8):
 
 
 def sample_rows(L, n_rand, seed, tile=128):
+    """The first and last query tile, a whole tile in the middle of the
+    sequence (mid-sequence causal tiles: many full key tiles, then the
+    diagonal), and n_rand random rows."""
     rng = np.random.default_rng(seed)
-    rows = set(range(min(L, tile))) | set(range(max(0, L - tile), L))
+    mid = (L // 2) // tile * tile
+    rows = set(range(min(L, tile))) | set(range(max(0, L - tile), L)) | set(range(mid, min(L, mid + tile)))
     rows |= set(rng.integers(0, L, size=n_rand).tolist())
     return np.array(sorted(rows))
 
