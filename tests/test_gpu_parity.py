@@ -342,3 +342,38 @@ def test_empty_inputs():
     qv = torch.zeros((0, 2, 64), dtype=torch.float16, device="cuda")
     o = S().attn(qv, qv, qv, cu_seqlens=cu, max_seqlen=0)
     assert o.shape == qv.shape
+
+
+@pytest.mark.parametrize("wl_name", ["TEXT", "VIDEO"])
+def test_packed_qkv_views_and_strided_output(wl_name):
+    """Q, K and V as views of one packed [B, N, 3, H, d] tensor (token stride
+    3·H·d) and O written into a slice of a wider buffer (token stride (H+1)·d):
+    bit-identical to contiguous tensors, causal and not, fp16 and FP8 P·V; the
+    buffer's other head slot is left as it was.  The SDPA drop-in on the
+    transposed [B, H, N, d] views of the packed tensor gives the same bits as on
+    their contiguous copies."""
+    wl = getattr(synth, wl_name)
+    inp = synth.generate(wl, seqlen=333, batch=2, heads=4)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    qkv = torch.stack([q, k, v], dim=2)
+    qv, kv, vv = qkv.unbind(2)
+    assert qv.stride(1) == 3 * q.shape[2] * q.shape[3]
+    B, N, H, D = q.shape
+    for causal in (False, True):
+        for pv in (S().SAGE_PV_FP16, S().SAGE_PV_FP8):
+            ref = S().attn(q, k, v, causal=causal, pv_mode=pv, blk_q=wl.blk_q, blk_k=wl.blk_k)
+            buf = torch.full((B, N, H + 1, D), 7.0, dtype=torch.float16, device="cuda")
+            out = buf[:, :, :H]
+            got = S().attn(qv, kv, vv, causal=causal, pv_mode=pv, blk_q=wl.blk_q, blk_k=wl.blk_k, out=out)
+            torch.cuda.synchronize()
+            assert got.data_ptr() == out.data_ptr()
+            assert torch.equal(got, ref), (causal, pv)
+            assert bool((buf[:, :, H] == 7.0).all())
+    qh, kh, vh = (t.transpose(1, 2) for t in (qv, kv, vv))
+    assert not qh.is_contiguous()
+    for causal in (False, True):
+        a = S().scaled_dot_product_attention(qh, kh, vh, is_causal=causal, blk_q=wl.blk_q, blk_k=wl.blk_k)
+        b = S().scaled_dot_product_attention(qh.contiguous(), kh.contiguous(), vh.contiguous(), is_causal=causal,
+                                             blk_q=wl.blk_q, blk_k=wl.blk_k)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), causal
