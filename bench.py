@@ -86,8 +86,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(attention shards by (sequence, head) with no communication; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(attention shards by (sequence, head) with no communication between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 
