@@ -52,6 +52,9 @@
  * Ownership.  The caller allocates every buffer (device memory) including
  *   the workspace; the library allocates and frees nothing on the device and
  *   keeps no pointer after returning.
+ * Aliasing.  No output of a call (O, codes, scales, means, the workspace)
+ *   may overlap any of its inputs or another of its outputs: the kernels
+ *   read and write them concurrently, and the library does not check.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  All work
  *   is enqueued asynchronously; nothing synchronises.  Buffers must stay
  *   valid until the stream has executed the work.
