@@ -968,7 +968,7 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   };
   auto mphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    if constexpr (!FP8 && D == 128) __builtin_amdgcn_s_setprio(0);
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(0);
     // Loads V(b+2), then K(b+4), of tiles owned by this half, as NOPS single
     // loads.  They are issued whether or not the tile exists (past the end
     // the descriptor is empty: nothing is read, the slot written holds a
@@ -1033,10 +1033,11 @@ __device__ __forceinline__ void attn_body(const Problem& p, const AttnArgs& a, l
   };
   auto vphase = [&](int b, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    // fp16 P.V at D = 128: the softmax wave gets the higher issue priority on
-    // its SIMD (about 1% on these kernels; at D = 64 and with FP8 P.V it is not
-    // faster, and giving the matrix wave the priority is 1-3% slower)
-    if constexpr (!FP8 && D == 128) __builtin_amdgcn_s_setprio(1);
+    // D = 128: the softmax wave gets the higher issue priority on its SIMD
+    // (about 1% on these kernels, 0.1-1.2% with FP8 P.V; at D = 64 it is not
+    // faster, and giving the matrix wave the priority is 1-3% slower, 11%
+    // with FP8 P.V)
+    if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
     const int t = b - 1;
     const Ck ck = load_ck(min(max(t, 0), ntiles - 1));  // (t outside the tiles: value unused)
     const uint32_t dslot = doffs(wrap6(pd + 5));         // tile t = b - 1 (smooth Q)
